@@ -1,0 +1,226 @@
+"""Benchmark of the local MoE forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one moe_forward call (route -> dispatch -> SwiGLU experts ->
+combine) over one batch of synthetic inputs already resident in HBM.  The
+default workload is the Mixtral-shaped bf16 layer (T=4096, H=4096, I=14336,
+E=8, top-2, renormalised).  W untimed steps, then K timed steps bracketed by
+device synchronisation; one JSON line on stdout.
+
+Per-kernel durations come from HIP events the library records around each of
+its kernels on the forward's stream (moe_set_timing_events), averaged over
+the K timed steps.  The roofline object describes the dominant kernel (the
+gate+up grouped GEMM with the SwiGLU epilogue).  The CPU baseline times the
+oracle (numpy) on a few tokens of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+KERNELS = ["route", "dispatch_count", "dispatch_scan", "dispatch_scatter",
+           "gateup_gemm", "down_gemm", "combine"]
+
+WORKLOADS = {
+    "mixtral": ("mixtral", None),
+    "fine": ("fine", None),
+    "decode32": ("decode", 32),
+    "decode256": ("decode", 256),
+}
+CPU_SAMPLE_TOKENS = {"mixtral": 3, "fine": 3, "decode32": 6, "decode256": 6}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mixtral", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic(wl, counts):
+    """Algorithmic work of each kernel for one forward (bytes moved or
+    FLOP), from the sizes and the routing histogram."""
+    T, H, I, E, k = wl["T"], wl["H"], wl["I"], wl["E"], wl["k"]
+    s = 2 if wl["fmt"] != "f32" else 4
+    sl = s
+    N = T * k
+    touched = int((counts > 0).sum())
+    w_gu = 2 * touched * I * H * s
+    w_d = touched * H * I * s
+    return {
+        "route": dict(bytes=T * E * sl + N * (4 + sl)),
+        "dispatch_count": dict(bytes=N * 4 * 2),
+        "dispatch_scan": dict(bytes=(E + 1) * 4),
+        "dispatch_scatter": dict(bytes=T * H * s + N * H * s + N * 4 * 5),
+        "gateup_gemm": dict(flop=4 * N * H * I,
+                            bytes=N * H * s + w_gu + N * I * s),
+        "down_gemm": dict(flop=2 * N * H * I,
+                          bytes=N * I * s + w_d + N * H * s),
+        "combine": dict(bytes=N * H * s + N * (4 + sl) + T * H * s),
+        "touched_experts": touched,
+    }
+
+
+def cpu_baseline(wl, name, tokens):
+    """The oracle, untuned, on a bounded sample of the workload's tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from mixture_experts_layer_28_amd import workloads
+    from oracle.moe import forward_tokens
+
+    fmt = wl["fmt"]
+    host = {key: workloads.to_numpy(wl[key], fmt)
+            for key in ("x", "logits", "w_gate", "w_up", "w_down")}
+    rng = np.random.default_rng(123)
+    sample = sorted(rng.choice(wl["T"], size=tokens, replace=False).tolist())
+    t0 = time.perf_counter()
+    forward_tokens(host["x"], host["logits"], host["w_gate"], host["w_up"],
+                   host["w_down"], wl["k"], wl["renorm"], fmt, sample)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d tokens (route, k experts, combine per token; "
+                      "numpy float64), %.1f s" % (tokens, wl["T"], dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (expert/data parallelism is described, not built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_28_amd as moe
+    from mixture_experts_layer_28_amd import _lib, workloads
+
+    dev = torch.device("cuda:0")
+    base, T = WORKLOADS[args.workload]
+    wl = workloads.make(base, T=T, device=dev)
+    T, H, I, E, k = wl["T"], wl["H"], wl["I"], wl["E"], wl["k"]
+    x, logits = wl["x"], wl["logits"]
+    wg, wu, wd = wl["w_gate"], wl["w_up"], wl["w_down"]
+
+    # routing histogram (outside the timed region): touched experts
+    idx, _ = moe.moe_route(logits, k, wl["renorm"])
+    d = moe.moe_dispatch(x, idx, E)
+    off = d["offsets"].cpu().numpy().astype(np.int64)
+    counts = np.diff(off)
+    del d, idx
+
+    ws_bytes = moe.moe_forward_workspace_size(T, H, I, E, k, x.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=x.dtype, device=dev)
+
+    def step():
+        moe.moe_forward(x, logits, wg, wu, wd, k, wl["renorm"], out=out,
+                        workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    stream = torch.cuda.current_stream(dev)
+    nev = _lib.lib()
+    marks = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        for ev in evs:
+            ev.record(stream)  # materialise the handles
+        marks.append(evs)
+    torch.cuda.synchronize(dev)
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        handles = (_lib.ctypes.c_void_p * 8)(*[ev.cuda_event for ev in marks[i]])
+        _lib.check(nev.moe_set_timing_events(handles, 8))
+        step()
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    _lib.check(nev.moe_set_timing_events(None, 0))
+
+    per_kernel = {name: 0.0 for name in KERNELS}
+    for evs in marks:
+        for j, name in enumerate(KERNELS):
+            per_kernel[name] += evs[j].elapsed_time(evs[j + 1])
+    per_kernel = {n: v / args.steps for n, v in per_kernel.items()}  # ms
+
+    alg = algorithmic(wl, counts)
+    stages = {}
+    for name in KERNELS:
+        ms = per_kernel[name]
+        st = {"ms": round(ms, 5)}
+        a = alg[name]
+        if "flop" in a:
+            st["tflops"] = round(a["flop"] / (ms * 1e-3) / 1e12, 2)
+        st["gbs"] = round(a["bytes"] / (ms * 1e-3) / 1e9, 1)
+        stages[name] = st
+
+    ms_step = elapsed / args.steps * 1e3
+    g = alg["gateup_gemm"]
+    g_ms = per_kernel["gateup_gemm"]
+    if base == "decode":
+        ach = g["bytes"] / (g_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "gateup_gemm"}
+    else:
+        ach = g["flop"] / (g_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "gateup_gemm"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.workload, CPU_SAMPLE_TOKENS[args.workload])
+
+    line = {
+        "metric": "MoE forward tokens/sec",
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl["fmt"] == "bf16" else wl["fmt"],
+        "data": "synthetic",
+        "config": {"workload": "%s bf16 T=%d H=%d I=%d E=%d top_k=%d "
+                               "renormalize=%s" % (base, T, H, I, E, k,
+                                                   wl["renorm"]),
+                   "T": T, "H": H, "I": I, "E": E, "top_k": k,
+                   "touched_experts": alg["touched_experts"],
+                   "flop_per_step": 6 * T * k * H * I},
+        "tflops_per_step": round(6 * T * k * H * I / (ms_step * 1e-3) / 1e12,
+                                 1),
+        "roofline": roof,
+        "stages": stages,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

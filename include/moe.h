@@ -1,0 +1,206 @@
+/*
+ * moe.h - C ABI of libmoe, a local Mixture-of-Experts forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation follows the ruDNN user guide (RUDA docs, German edition),
+ * sections 3-6 ("MoE workflow", "routing contract", "expert weights and
+ * dispatch", "calling MoE"), and the expert stage of the docs.rs page
+ * "ruDNN 0.1.25 source, src/moe/experts.rs" (SwiGluExperts::new,
+ * forward_dispatched_with_strategy, forward):
+ *
+ *   logits [T,E] -> FP32 softmax over all E + top-k -> compact dispatch
+ *   -> SwiGLU experts -> weighted combine -> out [T,H]
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer on the current HIP device,
+ *   to a dense row-major array (the shapes below list the dimensions
+ *   outermost first).  The caller allocates and owns all memory; the library
+ *   borrows pointers for the duration of the call and allocates nothing.
+ * - All work is enqueued on `stream` (a hipStream_t; NULL means the default
+ *   stream).  No call synchronises the stream or reads device memory on the
+ *   host: results are ready when the stream reaches them.
+ * - Every argument check runs on the host BEFORE anything is enqueued.  A
+ *   failed check returns a nonzero moe_status and enqueues nothing;
+ *   moe_last_error() then describes it.  A failed kernel launch returns
+ *   MOE_ERR_HIP.  There is no fallback to another path on any error.
+ * - NaN and infinity in the data are not errors: they propagate as the
+ *   routing contract describes (guide, section 4).
+ * - T == 0 (or N == 0) is valid and enqueues nothing.
+ * - Outputs must not overlap inputs or each other.
+ * - Sizes are int64_t; T*top_k must be below 2^32 (row ids are uint32) and
+ *   every array size in bytes must fit in int64_t.
+ * - Element types: moe_dtype.  Activations, expert weights and expert
+ *   outputs share one dtype `dt`; logits and routing weights share `ldt`
+ *   (the guide admits F32, F16 and BF16 for both).
+ */
+#ifndef MOE_MI355X_MOE_H
+#define MOE_MI355X_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,
+    MOE_F16 = 1,
+    MOE_BF16 = 2
+} moe_dtype;
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null pointer, top_k out of range, ...   */
+    MOE_ERR_SHAPE = 2,       /* a size is zero/negative or overflows     */
+    MOE_ERR_DTYPE = 3,       /* unknown dtype code                        */
+    MOE_ERR_UNSUPPORTED = 4, /* valid but beyond this library's limits    */
+    MOE_ERR_HIP = 5          /* a HIP launch failed                        */
+} moe_status;
+
+/*
+ * moe_route - softmax/top-k routing (guide, section 4 "routing contract").
+ *
+ *   logits  [T,E]      ldt     input
+ *   idx     [T,top_k]  uint32  output: selected experts, best first
+ *   weights [T,top_k]  ldt     output: routing weights
+ *
+ * Per row: the softmax is taken over all E experts in FP32; experts are
+ * ranked by logit (descending) with ties going to the lower expert id, and
+ * the first top_k are taken in that order.  With renormalize != 0 the
+ * selected probabilities are divided by their FP32 sum.  The weights are
+ * then rounded (nearest even) to ldt.  A row holding a NaN, a +inf, or only
+ * -inf gets weights NaN and indices 0..top_k-1.
+ * Requires 1 <= top_k <= E.  E <= 65536.
+ */
+int moe_route(const void* logits, int ldt, int64_t T, int64_t E,
+              int64_t top_k, int renormalize, uint32_t* idx, void* weights,
+              void* stream);
+
+/*
+ * moe_dispatch_workspace_size - bytes of scratch moe_dispatch needs for
+ * (T, E, top_k).  Pure host arithmetic; returns 0 for invalid sizes.
+ */
+size_t moe_dispatch_workspace_size(int64_t T, int64_t E, int64_t top_k);
+
+/*
+ * moe_dispatch - compact expert-contiguous dispatch (guide, section 5).
+ *
+ *   x          [T,H]      dt      input token rows
+ *   idx        [T,top_k]  uint32  input: expert of each (token, slot)
+ *   xd         [N,H]      dt      output: dispatched rows, N = T*top_k
+ *   offsets    [E+1]      uint32  output: expert e owns rows
+ *                                 [offsets[e], offsets[e+1])
+ *   row_expert [N]        uint32  output: expert of each dispatched row
+ *   row_token  [N]        uint32  output: source token of each row
+ *   token_row  [T,top_k]  uint32  output: the dispatched row of each
+ *                                 (token, slot): the stored mapping that
+ *                                 restores token order
+ *   workspace  moe_dispatch_workspace_size(T,E,top_k) bytes of scratch
+ *
+ * No token is dropped: offsets[E] == N and every row is a bit copy of its
+ * token.  Inside an expert, rows follow (token, slot) order (the guide
+ * leaves that order open; this library keeps it stable and deterministic).
+ * idx values must be < E.  An out-of-range value is not read as an expert:
+ * its rows are placed after offsets[E] with row_expert 0xFFFFFFFF (so
+ * offsets[E] < N signals it), every access stays in bounds, and
+ * moe_experts_forward writes zeros for those rows.
+ */
+int moe_dispatch(const void* x, int dt, int64_t T, int64_t H, int64_t E,
+                 int64_t top_k, const uint32_t* idx, void* xd,
+                 uint32_t* offsets, uint32_t* row_expert, uint32_t* row_token,
+                 uint32_t* token_row, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * moe_experts_forward - SwiGLU experts over expert segments (experts page,
+ * forward_dispatched_with_strategy; weight layouts from SwiGluExperts::new).
+ *
+ *   xd      [N,H]    dt      dispatched rows
+ *   w_gate  [E,I,H]  dt      gate weights (no bias)
+ *   w_up    [E,I,H]  dt      up weights (no bias)
+ *   w_down  [E,H,I]  dt      down weights (no bias)
+ *   offsets [E+1]    uint32  segments as written by moe_dispatch
+ *   act     [N,I]    dt      output/scratch: SiLU(gate) * up
+ *   y       [N,H]    dt      output: expert output rows
+ *
+ * For a row r of segment e:  g = xd[r] . w_gate[e]^T,  u = xd[r] . w_up[e]^T
+ * (FP32 accumulation, each rounded to dt), act = SiLU(g) * u (FP32, rounded
+ * to dt), y[r] = act . w_down[e]^T (FP32 accumulation, rounded to dt).
+ * Segments must be monotone with offsets[0] == 0 and offsets[E] <= N; rows
+ * in [offsets[E], N) get y = 0.
+ */
+int moe_experts_forward(const void* xd, int dt, int64_t N, int64_t H,
+                        int64_t I, int64_t E, const void* w_gate,
+                        const void* w_up, const void* w_down,
+                        const uint32_t* offsets, void* act, void* y,
+                        void* stream);
+
+/*
+ * moe_combine - weighted merge back into token order (guide, section 6).
+ *
+ *   y         [N,H]      dt      expert output rows
+ *   weights   [T,top_k]  wdt     routing weights
+ *   token_row [T,top_k]  uint32  mapping written by moe_dispatch
+ *   out       [T,H]      dt      output
+ *
+ * out[t] = sum over slots j = 0..top_k-1, in slot order and in FP32, of
+ * weights[t,j] * y[token_row[t,j]], rounded once to dt.  The routing
+ * weights are applied here and nowhere else.  token_row values must be < N.
+ */
+int moe_combine(const void* y, int dt, int64_t N, int64_t T, int64_t H,
+                int64_t top_k, const void* weights, int wdt,
+                const uint32_t* token_row, void* out, void* stream);
+
+/*
+ * moe_forward_workspace_size - bytes of scratch moe_forward needs.
+ * Returns 0 for invalid arguments.
+ */
+size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E,
+                                  int64_t top_k, int dt, int ldt);
+
+/*
+ * moe_forward - the whole local MoE forward (experts page,
+ * SwiGluExperts::forward): moe_route -> moe_dispatch ->
+ * moe_experts_forward -> moe_combine on one stream.
+ *
+ *   x      [T,H]   dt    input tokens
+ *   logits [T,E]   ldt   router logits, computed by the caller
+ *   w_gate, w_up [E,I,H], w_down [E,H,I]   dt
+ *   out    [T,H]   dt    output
+ *   workspace  moe_forward_workspace_size(...) bytes, 256-byte aligned
+ */
+int moe_forward(const void* x, int dt, const void* logits, int ldt,
+                int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                int renormalize, const void* w_gate, const void* w_up,
+                const void* w_down, void* out, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * moe_set_timing_events - instrumentation for measuring each kernel.
+ *
+ * events: `count` hipEvent_t handles created by the caller (hipEventCreate),
+ * or NULL with count 0 to switch recording off.  While set, every
+ * moe_forward call on this thread records events[0] on its stream before
+ * its first kernel and events[i] right after its i-th kernel, so the
+ * elapsed time between events[i-1] and events[i] is kernel i.  The kernels
+ * of moe_forward, in order: 1 route, 2 dispatch count, 3 dispatch scan,
+ * 4 dispatch scatter, 5 gate+up GEMM with SwiGLU, 6 down GEMM, 7 combine.
+ * count must be 0 or MOE_TIMING_EVENTS.  The library does not own the
+ * events; the caller keeps them alive while recording is on.
+ */
+#define MOE_TIMING_EVENTS 8
+int moe_set_timing_events(void* const* events, int count);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_MOE_H */

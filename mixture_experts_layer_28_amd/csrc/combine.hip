@@ -1,0 +1,136 @@
+// Combine kernel: weighted merge of the expert rows back into token order.
+//
+// Contract: ruDNN user guide (RUDA docs), section 6 "calling MoE": combine
+// uses the dispatch mapping to restore token order and merges the expert
+// outputs with the routing weights.  The weights are applied here only
+// (section 12 states that the dispatch backward does not apply them again).
+//
+// out[t] = sum_{j<k} w[t,j] * y[token_row[t,j]], FP32 fused multiply-adds in
+// slot order, rounded once to the activation dtype.  A workgroup takes a
+// run of tokens; their k row ids and weights are staged in LDS, then the
+// 256 threads stream 16-byte vectors of every row (HBM bound: N*H reads,
+// T*H writes).  A row id >= N contributes NaN instead of being read.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+template <int D> struct Vec;  // 16-byte vectors of each storage type
+template <> struct Vec<DT_F32> { static constexpr int n = 4; };
+template <> struct Vec<DT_F16> { static constexpr int n = 8; };
+template <> struct Vec<DT_BF16> { static constexpr int n = 8; };
+
+template <int D, int WD, int NV>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const typename Storage<D>::T* __restrict__ y, int64_t N, int64_t T,
+    int64_t H, int k, const typename Storage<WD>::T* __restrict__ w,
+    const uint32_t* __restrict__ token_row,
+    typename Storage<D>::T* __restrict__ out, int tpb) {
+  using S = typename Storage<D>::T;
+  extern __shared__ uint32_t sm[];
+  uint32_t* srow = sm;
+  float* sw = (float*)(sm + tpb * k);
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  for (int q = threadIdx.x; q < tpb * k; q += blockDim.x) {
+    const int64_t t = t0 + q / k;
+    if (t < T) {
+      srow[q] = token_row[t0 * k + q];
+      sw[q] = to_f32<WD>(w[t0 * k + q]);
+    }
+  }
+  __syncthreads();
+  const int64_t vpr = H / NV;  // vectors per row (NV elements each)
+  const int64_t total = (int64_t)tpb * vpr;
+  for (int64_t q = threadIdx.x; q < total; q += blockDim.x) {
+    const int tl = (int)(q / vpr);
+    const int64_t v = q - (int64_t)tl * vpr;
+    const int64_t t = t0 + tl;
+    if (t >= T) break;
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t r = srow[tl * k + j];
+      const float wt = sw[tl * k + j];
+      if (r < (uint64_t)N) {
+        S vals[NV];
+        if constexpr (NV * sizeof(S) == 16) {
+          *(uint4*)vals = *(const uint4*)(y + (int64_t)r * H + v * NV);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NV; ++i) vals[i] = y[(int64_t)r * H + v * NV + i];
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] = fmaf(wt, to_f32<D>(vals[i]), acc[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] = __builtin_nanf("");
+      }
+    }
+    S res[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) res[i] = from_f32<D>(acc[i]);
+    if constexpr (NV * sizeof(S) == 16) {
+      *(uint4*)(out + t * H + v * NV) = *(const uint4*)res;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) out[t * H + v * NV + i] = res[i];
+    }
+  }
+}
+
+template <int D, int WD>
+hipError_t launch_c(const void* y, int64_t N, int64_t T, int64_t H, int k,
+                    const void* w, const uint32_t* token_row, void* out,
+                    hipStream_t st) {
+  using S = typename Storage<D>::T;
+  using SW = typename Storage<WD>::T;
+  constexpr int NV = Vec<D>::n;
+  const bool vec_ok = H % NV == 0 && ((uintptr_t)y % 16 == 0) &&
+                      ((uintptr_t)out % 16 == 0);
+  const int64_t vpr = vec_ok ? H / NV : H;
+  int64_t tpb = 1024 / vpr;
+  if (tpb < 1) tpb = 1;
+  if (tpb * k > 2048) tpb = 2048 / k;
+  if (tpb < 1) tpb = 1;
+  const dim3 grid((unsigned)((T + tpb - 1) / tpb));
+  const size_t lds = (size_t)tpb * k * 8;
+  if (vec_ok) {
+    hipLaunchKernelGGL((combine_kernel<D, WD, NV>), grid, dim3(256), lds, st,
+                       (const S*)y, N, T, H, k, (const SW*)w, token_row,
+                       (S*)out, (int)tpb);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<D, WD, 1>), grid, dim3(256), lds, st,
+                       (const S*)y, N, T, H, k, (const SW*)w, token_row,
+                       (S*)out, (int)tpb);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_cw(const void* y, int64_t N, int64_t T, int64_t H, int k,
+                     const void* w, int wdt, const uint32_t* token_row,
+                     void* out, hipStream_t st) {
+  switch (wdt) {
+    case DT_F32: return launch_c<D, DT_F32>(y, N, T, H, k, w, token_row, out, st);
+    case DT_F16: return launch_c<D, DT_F16>(y, N, T, H, k, w, token_row, out, st);
+    default: return launch_c<D, DT_BF16>(y, N, T, H, k, w, token_row, out, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, int dt, int64_t N, int64_t T,
+                          int64_t H, int k, const void* w, int wdt,
+                          const uint32_t* token_row, void* out,
+                          hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return launch_cw<DT_F32>(y, N, T, H, k, w, wdt, token_row, out, st);
+    case DT_F16: return launch_cw<DT_F16>(y, N, T, H, k, w, wdt, token_row, out, st);
+    default: return launch_cw<DT_BF16>(y, N, T, H, k, w, wdt, token_row, out, st);
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,212 @@
+// Dispatch kernels: expert histogram -> scan -> scatter.
+//
+// Contract: ruDNN user guide (RUDA docs), section 5 "expert weights and
+// dispatch": no token is dropped for a capacity limit, and a stored mapping
+// restores token order.  The experts page (docs.rs "ruDNN 0.1.25 source,
+// src/moe/experts.rs", forward_dispatched_with_strategy) consumes complete,
+// monotone expert segments.
+//
+// The N = T*k (token, slot) entries are cut into chunks; each chunk is one
+// wavefront's sequential job, which makes the order inside every expert
+// segment the stable (token, slot) order without global atomics:
+//   1. count:   per chunk, per expert: how many entries, and each entry's
+//               rank among the chunk's entries of the same expert (a ballot
+//               per distinct expert in each 64-entry group).
+//   2. scan:    one workgroup turns the [chunk][expert] counts into segment
+//               offsets and, in place, into each chunk's first row per expert.
+//   3. scatter: each token row is read once and written to its k rows
+//               (16-byte vector copies), and the mapping arrays are written.
+// Expert ids >= E go to an extra bin E placed after offsets[E].
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxTable = 1 << 20;  // u32 entries of the count table
+
+__global__ void dispatch_count_kernel(const uint32_t* __restrict__ idx,
+                                      int64_t N, int E, int64_t chunk,
+                                      int64_t nchunks, int waves,
+                                      uint32_t* __restrict__ table,
+                                      uint32_t* __restrict__ local_rank) {
+  extern __shared__ uint32_t cnt_all[];
+  const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int64_t c = (int64_t)blockIdx.x * waves + wv;
+  if (c >= nchunks) return;  // uniform per wave; no block barrier below
+  const int nb = E + 1;
+  uint32_t* cnt = cnt_all + wv * nb;
+  for (int b = lane; b < nb; b += 64) cnt[b] = 0u;
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int64_t i0 = c * chunk;
+  const int64_t i1 = (i0 + chunk < N) ? i0 + chunk : N;
+  for (int64_t g = i0; g < i1; g += 64) {
+    const int64_t i = g + lane;
+    const bool valid = i < i1;
+    uint32_t e = valid ? idx[i] : 0u;
+    if (e > (uint32_t)E) e = (uint32_t)E;
+    uint64_t todo = __ballot(valid);
+    uint32_t rank = 0;
+    while (todo) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)e, leader);
+      const bool mine = valid && e == v;
+      const uint64_t m = __ballot(mine);
+      uint32_t old = 0;
+      if (lane == leader) {
+        old = cnt[v];
+        cnt[v] = old + (uint32_t)__popcll(m);
+      }
+      old = (uint32_t)__builtin_amdgcn_readlane((int)old, leader);
+      if (mine) rank = old + (uint32_t)__popcll(m & lt);
+      todo &= ~m;
+    }
+    if (valid) local_rank[i] = rank;
+  }
+  for (int b = lane; b < nb; b += 64) table[c * nb + b] = cnt[b];
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    uint32_t* __restrict__ table, int64_t nchunks, int E,
+    uint32_t* __restrict__ offsets) {
+  __shared__ uint32_t sh[1024];
+  const int tid = threadIdx.x;
+  const int nb = E + 1;
+  const int per = (nb + 1023) / 1024;
+  const int b0 = tid * per < nb ? tid * per : nb;
+  const int b1 = b0 + per < nb ? b0 + per : nb;
+  uint32_t mine = 0;
+  for (int b = b0; b < b1; ++b)
+    for (int64_t c = 0; c < nchunks; ++c) mine += table[c * nb + b];
+  sh[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t add = tid >= off ? sh[tid - off] : 0u;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  uint32_t run = sh[tid] - mine;  // exclusive prefix over bins
+  for (int b = b0; b < b1; ++b) {
+    offsets[b] = run;  // bins 0..E: offsets[E] is the first invalid row
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const uint32_t n = table[c * nb + b];
+      table[c * nb + b] = run;
+      run += n;
+    }
+  }
+}
+
+template <typename V>
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const V* __restrict__ x, V* __restrict__ xd, int64_t T, int64_t vpr,
+    int k, int E, int64_t chunk, const uint32_t* __restrict__ idx,
+    const uint32_t* __restrict__ table, uint32_t* __restrict__ token_row,
+    uint32_t* __restrict__ row_expert, uint32_t* __restrict__ row_token,
+    int tpb) {
+  extern __shared__ uint32_t dst[];
+  const int nb = E + 1;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  for (int q = threadIdx.x; q < tpb * k; q += blockDim.x) {
+    const int64_t t = t0 + q / k;
+    if (t < T) {
+      const int64_t i = t0 * k + q;
+      const uint32_t e = idx[i];
+      const uint32_t bin = e < (uint32_t)E ? e : (uint32_t)E;
+      const uint32_t r = table[(i / chunk) * nb + bin] + token_row[i];
+      token_row[i] = r;
+      row_expert[r] = e < (uint32_t)E ? e : 0xffffffffu;
+      row_token[r] = (uint32_t)t;
+      dst[q] = r;
+    }
+  }
+  __syncthreads();
+  const int64_t total = (int64_t)tpb * vpr;
+  for (int64_t q = threadIdx.x; q < total; q += blockDim.x) {
+    const int tl = (int)(q / vpr);
+    const int64_t v = q - (int64_t)tl * vpr;
+    const int64_t t = t0 + tl;
+    if (t >= T) break;  // q only grows
+    const V val = x[t * vpr + v];
+    for (int j = 0; j < k; ++j) xd[(int64_t)dst[tl * k + j] * vpr + v] = val;
+  }
+}
+
+template <typename V>
+hipError_t launch_scatter(const void* x, void* xd, int64_t T, int64_t bytes,
+                          int k, int E, int64_t chunk, const uint32_t* idx,
+                          const uint32_t* table, uint32_t* token_row,
+                          uint32_t* row_expert, uint32_t* row_token,
+                          hipStream_t st) {
+  const int64_t vpr = bytes / (int64_t)sizeof(V);
+  int64_t tpb = 1024 / vpr;
+  if (tpb < 1) tpb = 1;
+  if (tpb * k > 4096) tpb = 4096 / k;
+  if (tpb < 1) tpb = 1;
+  const dim3 grid((unsigned)((T + tpb - 1) / tpb));
+  const size_t lds = (size_t)tpb * k * sizeof(uint32_t);
+  hipLaunchKernelGGL((dispatch_scatter_kernel<V>), grid, dim3(256), lds, st,
+                     (const V*)x, (V*)xd, T, vpr, k, E, chunk, idx, table,
+                     token_row, row_expert, row_token, (int)tpb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+DispatchPlan plan_dispatch(int64_t T, int64_t E, int64_t k) {
+  DispatchPlan p;
+  p.N = T * k;
+  p.chunk = 256;
+  p.nchunks = (p.N + p.chunk - 1) / p.chunk;
+  while (p.nchunks * (E + 1) > kMaxTable && p.chunk < (1 << 20)) {
+    p.chunk *= 2;
+    p.nchunks = (p.N + p.chunk - 1) / p.chunk;
+  }
+  int waves = (int)(16384 / (E + 1));
+  p.waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+  p.table_bytes = (size_t)(p.nchunks * (E + 1)) * sizeof(uint32_t);
+  return p;
+}
+
+hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,
+                           int E, int k, const uint32_t* idx, void* xd,
+                           uint32_t* offsets, uint32_t* row_expert,
+                           uint32_t* row_token, uint32_t* token_row,
+                           void* workspace, const DispatchPlan& p,
+                           hipStream_t st) {
+  uint32_t* table = (uint32_t*)workspace;
+  if (p.nchunks > 0) {
+    const dim3 grid((unsigned)((p.nchunks + p.waves - 1) / p.waves));
+    const size_t lds = (size_t)p.waves * (E + 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL(dispatch_count_kernel, grid, dim3(64 * p.waves), lds,
+                       st, idx, p.N, E, p.chunk, p.nchunks, p.waves, table,
+                       token_row);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  timing_mark(2, st);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, table,
+                     p.nchunks, E, offsets);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || T == 0) return err;  // T == 0: all offsets 0
+  timing_mark(3, st);
+
+  const int64_t es = dt == DT_F32 ? 4 : 2;
+  const int64_t bytes = H * es;
+  const uintptr_t al = (uintptr_t)x | (uintptr_t)xd;
+  if (bytes % 16 == 0 && al % 16 == 0)
+    return launch_scatter<uint4>(x, xd, T, bytes, k, E, p.chunk, idx, table,
+                                 token_row, row_expert, row_token, st);
+  if (bytes % 8 == 0 && al % 8 == 0)
+    return launch_scatter<uint2>(x, xd, T, bytes, k, E, p.chunk, idx, table,
+                                 token_row, row_expert, row_token, st);
+  if (bytes % 4 == 0 && al % 4 == 0)
+    return launch_scatter<uint32_t>(x, xd, T, bytes, k, E, p.chunk, idx,
+                                    table, token_row, row_expert, row_token,
+                                    st);
+  return launch_scatter<uint16_t>(x, xd, T, bytes, k, E, p.chunk, idx, table,
+                                  token_row, row_expert, row_token, st);
+}
+
+}  // namespace moe

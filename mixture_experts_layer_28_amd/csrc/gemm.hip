@@ -1,0 +1,478 @@
+// Segmented grouped GEMMs of the SwiGLU experts.
+//
+// Source: docs.rs "ruDNN 0.1.25 source, src/moe/experts.rs".
+// SwiGluExperts::new fixes bias-free gate/up weights [E,I,H] and down
+// weights [E,H,I]; forward_dispatched_with_strategy computes, per expert
+// segment of the dispatched rows, gate = X W_gate^T and up = X W_up^T (both
+// "NT": every operand is contiguous along the reduction axis), overwrites
+// gate with SiLU(gate) * up, and multiplies the result by W_down^T.
+//
+// Here the two first products share one kernel: a tile of output columns
+// [n0, n0 + BN/2) loads BN/2 rows of W_gate and the same BN/2 rows of W_up,
+// so every lane holds gate and up for the same (row, column) and applies
+// SiLU(g) * u in the epilogue (g and u are rounded to the storage dtype
+// first, as the reference stores them, then SiLU runs in FP32).  The down
+// product is a second launch of the same kernel without the epilogue.
+//
+// Tiles: the grid covers an upper bound of the (expert, row block, column
+// block) tiles, (ceil(N/BM) + segments) * column blocks, so no host sync is
+// needed; each workgroup finds its tile from the device-side offsets (a
+// prefix sum over the segments done by one wavefront) and exits if it has
+// none.  Logical tile order is expert-major, then column block, then row
+// block, so consecutive tiles share a weight tile; consecutive logical ids
+// are kept on one XCD so they share that XCD's L2.
+//
+// MFMA path (bf16/f16, K a multiple of 8, 16-byte aligned operands):
+// 256 threads = 4 wavefronts in a WGM x (4/WGM) grid; v_mfma_f32_16x16x32
+// (bf16 or f16) with FP32 accumulators; K steps of 64 staged through a
+// double-buffered LDS tile whose 16-byte chunks are XOR-swizzled by row so
+// the fragment reads (16 rows, one chunk) spread over the banks; the next
+// K step's global loads are in flight while the current one is computed.
+//
+// Generic path (fp32, or shapes the MFMA path does not take): a 64x64 LDS
+// tiled FMA kernel with element-wise bounds checks.
+//
+// A segment s = E (rows [offsets[E], N), produced by out-of-range expert
+// ids) is written as zeros by the down launch.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+struct TileInfo {
+  int64_t lo, hi, row0;
+  int e, col, found;
+};
+
+// Executed by the 64 lanes of wavefront 0.  Segment s < E is
+// [offsets[s], offsets[s+1]); segment E (only if nseg > E) is
+// [offsets[E], N).  Bounds are clamped into [0, N] and made monotone so
+// that any offsets array keeps every access in bounds.
+__device__ void locate_tile(uint32_t L, const uint32_t* __restrict__ offsets,
+                            int E, int64_t N, int BM, uint32_t ncol, int nseg,
+                            TileInfo* ti) {
+  const int lane = threadIdx.x;
+  if (lane == 0) ti->found = 0;
+  uint32_t base = 0;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    const int s = s0 + lane;
+    int64_t lo = 0, hi = 0;
+    if (s < nseg) {
+      lo = offsets[s];
+      lo = lo < N ? lo : N;
+      hi = s < E ? (int64_t)offsets[s + 1] : N;
+      hi = hi < lo ? lo : (hi > N ? N : hi);
+    }
+    const uint32_t nt = (uint32_t)((hi - lo + BM - 1) / BM);
+    const uint32_t cnt = nt * ncol;
+    uint32_t inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
+    }
+    const uint32_t exc = inc - cnt;
+    const bool hit = L >= base + exc && L < base + inc;
+    if (__ballot(hit)) {
+      if (hit) {
+        const uint32_t local = L - base - exc;
+        ti->e = s;
+        ti->lo = lo;
+        ti->hi = hi;
+        ti->col = (int)(local / nt);
+        ti->row0 = lo + (int64_t)(local % nt) * BM;
+        ti->found = 1;
+      }
+      return;
+    }
+    base += __shfl(inc, 63, 64);
+  }
+}
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int D> struct Frag;
+template <> struct Frag<DT_BF16> {
+  using V = bf16x8;
+  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Frag<DT_F16> {
+  using V = f16x8;
+  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+template <int D, int BM, int BN, int WGM, bool GATEUP>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(
+    const typename Storage<D>::T* __restrict__ A,
+    const typename Storage<D>::T* __restrict__ B0,
+    const typename Storage<D>::T* __restrict__ B1,
+    typename Storage<D>::T* __restrict__ C,
+    const uint32_t* __restrict__ offsets, int64_t N, int K, int NB, int E,
+    uint32_t ncol, int nseg) {
+  using S = typename Storage<D>::T;
+  using V = typename Frag<D>::V;
+  constexpr int BK = 64;
+  constexpr int WGN = 4 / WGM;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int TCOLS = GATEUP ? BN / 2 : BN;  // output columns per tile
+  constexpr int CA = BM * 8 / 256, CB = BN * 8 / 256;
+  static_assert(CA >= 1 && CB >= 1 && FM >= 1 && FN >= (GATEUP ? 2 : 1), "tile");
+
+  __shared__ __attribute__((aligned(16))) S As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) S Bs[2][BN * BK];
+  __shared__ TileInfo ti;
+
+  const int tid = threadIdx.x;
+  const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
+  if (tid < 64) locate_tile(L, offsets, E, N, BM, ncol, nseg, &ti);
+  __syncthreads();
+  if (!ti.found) return;
+  const int e = ti.e;
+  const int64_t hi = ti.hi, row0 = ti.row0;
+  const int64_t n0 = (int64_t)ti.col * TCOLS;
+
+  if (e >= E) {  // rows of out-of-range experts: zeros
+    for (int q = tid; q < BM * TCOLS; q += 256) {
+      const int64_t r = row0 + q / TCOLS, c = n0 + q % TCOLS;
+      if (r < hi && c < NB) C[r * NB + c] = from_f32<D>(0.0f);
+    }
+    return;
+  }
+
+  // global source of each 16-byte chunk this thread stages
+  const S* pa[CA];
+  const S* pb[CB];
+  int ka[CA], kb[CB];
+#pragma unroll
+  for (int it = 0; it < CA; ++it) {
+    const int q = tid + 256 * it, r = q >> 3, ch = q & 7;
+    int64_t gr = row0 + r;
+    gr = gr < hi ? gr : hi - 1;
+    pa[it] = A + gr * K + ch * 8;
+    ka[it] = ch * 8;
+  }
+#pragma unroll
+  for (int it = 0; it < CB; ++it) {
+    const int q = tid + 256 * it, r = q >> 3, ch = q & 7;
+    const S* base = B0;
+    int64_t br = n0 + r;
+    if (GATEUP && r >= BN / 2) {
+      base = B1;
+      br = n0 + r - BN / 2;
+    }
+    br = br < NB ? br : NB - 1;
+    pb[it] = base + ((int64_t)e * NB + br) * K + ch * 8;
+    kb[it] = ch * 8;
+  }
+
+  u32x4 ra[CA], rb[CB];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < CA; ++it)
+      ra[it] = (k0 + ka[it] < K) ? *(const u32x4*)(pa[it] + k0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int it = 0; it < CB; ++it)
+      rb[it] = (k0 + kb[it] < K) ? *(const u32x4*)(pb[it] + k0) : u32x4{0, 0, 0, 0};
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int it = 0; it < CA; ++it) {
+      const int q = tid + 256 * it, r = q >> 3, ch = q & 7;
+      *(u32x4*)&As[st][r * BK + ((ch ^ swz(r)) << 3)] = ra[it];
+    }
+#pragma unroll
+    for (int it = 0; it < CB; ++it) {
+      const int q = tid + 256 * it, r = q >> 3, ch = q & 7;
+      *(u32x4*)&Bs[st][r * BK + ((ch ^ swz(r)) << 3)] = rb[it];
+    }
+  };
+
+  const int wid = tid >> 6, lane = tid & 63;
+  const int wm = wid / WGN, wn = wid % WGN;
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int arow[FM], brow[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) arow[i] = wm * WTM + i * 16 + (lane & 15);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (GATEUP) {
+      constexpr int H2 = FN / 2;
+      brow[j] = (j < H2 ? wn * (WTN / 2) + j * 16
+                        : BN / 2 + wn * (WTN / 2) + (j - H2) * 16) +
+                (lane & 15);
+    } else {
+      brow[j] = wn * WTN + j * 16 + (lane & 15);
+    }
+  }
+
+  const int nk = (K + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+      V a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = *(const V*)&As[st][arow[i] * BK + ((c ^ swz(arow[i])) << 3)];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        b[j] = *(const V*)&Bs[st][brow[j] * BK + ((c ^ swz(brow[j])) << 3)];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = Frag<D>::mma(a[i], b[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) store(st ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each fragment
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t r = row0 + wm * WTM + i * 16 + (lane >> 4) * 4 + q;
+      if (r >= hi) continue;
+      S* crow = C + r * NB;
+      if (GATEUP) {
+        constexpr int H2 = FN / 2;
+#pragma unroll
+        for (int j = 0; j < H2; ++j) {
+          const int64_t c = n0 + wn * (WTN / 2) + j * 16 + (lane & 15);
+          if (c < NB) {
+            const float g = to_f32<D>(from_f32<D>(acc[i][j][q]));
+            const float u = to_f32<D>(from_f32<D>(acc[i][j + H2][q]));
+            crow[c] = from_f32<D>(silu_mul(g, u));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t c = n0 + wn * WTN + j * 16 + (lane & 15);
+          if (c < NB) crow[c] = from_f32<D>(acc[i][j][q]);
+        }
+      }
+    }
+  }
+}
+
+// Generic FMA path: 64 x 64 tile (gate+up: 32 output columns), K step 16.
+template <int D, bool GATEUP>
+__global__ __launch_bounds__(256) void gemm_generic_kernel(
+    const typename Storage<D>::T* __restrict__ A,
+    const typename Storage<D>::T* __restrict__ B0,
+    const typename Storage<D>::T* __restrict__ B1,
+    typename Storage<D>::T* __restrict__ C,
+    const uint32_t* __restrict__ offsets, int64_t N, int K, int NB, int E,
+    uint32_t ncol, int nseg) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  constexpr int TCOLS = GATEUP ? 32 : 64;
+  __shared__ float As[BK][BM + 1];
+  __shared__ float Bs[BK][BN + 1];
+  __shared__ TileInfo ti;
+  const int tid = threadIdx.x;
+  const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
+  if (tid < 64) locate_tile(L, offsets, E, N, BM, ncol, nseg, &ti);
+  __syncthreads();
+  if (!ti.found) return;
+  const int e = ti.e;
+  const int64_t hi = ti.hi, row0 = ti.row0;
+  const int64_t n0 = (int64_t)ti.col * TCOLS;
+  if (e >= E) {
+    for (int q = tid; q < BM * TCOLS; q += 256) {
+      const int64_t r = row0 + q / TCOLS, c = n0 + q % TCOLS;
+      if (r < hi && c < NB) C[r * NB + c] = from_f32<D>(0.0f);
+    }
+    return;
+  }
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+  for (int k0 = 0; k0 < K; k0 += BK) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int q = tid + 256 * it, m = q / BK, kk = q % BK;
+      int64_t gr = row0 + m;
+      gr = gr < hi ? gr : hi - 1;
+      As[kk][m] = (k0 + kk < K) ? to_f32<D>(A[gr * K + k0 + kk]) : 0.0f;
+      int64_t br;
+      const typename Storage<D>::T* base = B0;
+      if (GATEUP) {
+        br = n0 + (m < 32 ? m : m - 32);
+        if (m >= 32) base = B1;
+      } else {
+        br = n0 + m;
+      }
+      br = br < NB ? br : NB - 1;
+      Bs[kk][m] = (k0 + kk < K)
+                      ? to_f32<D>(base[((int64_t)e * NB + br) * K + k0 + kk])
+                      : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+      if (GATEUP) {
+        b[0] = Bs[kk][tx * 2];
+        b[1] = Bs[kk][tx * 2 + 1];
+        b[2] = Bs[kk][32 + tx * 2];
+        b[3] = Bs[kk][32 + tx * 2 + 1];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = row0 + ty * 4 + i;
+    if (r >= hi) continue;
+    if (GATEUP) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t c = n0 + tx * 2 + j;
+        if (c < NB) {
+          const float g = to_f32<D>(from_f32<D>(acc[i][j]));
+          const float u = to_f32<D>(from_f32<D>(acc[i][j + 2]));
+          C[r * NB + c] = from_f32<D>(silu_mul(g, u));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t c = n0 + tx * 4 + j;
+        if (c < NB) C[r * NB + c] = from_f32<D>(acc[i][j]);
+      }
+    }
+  }
+}
+
+inline uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+template <int D, int BM, int BN, int WGM>
+hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
+                            int E, const void* wg, const void* wu,
+                            const void* wd, const uint32_t* offsets,
+                            void* act, void* y, hipStream_t st) {
+  using S = typename Storage<D>::T;
+  {
+    const uint32_t ncol = cdiv(I, BN / 2);
+    const uint32_t grid = ncol * (cdiv(N, BM) + (uint32_t)E);
+    hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, true>), dim3(grid),
+                       dim3(256), 0, st, (const S*)xd, (const S*)wg,
+                       (const S*)wu, (S*)act, offsets, N, (int)H, (int)I, E,
+                       ncol, E);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  timing_mark(5, st);
+  const uint32_t ncol = cdiv(H, BN);
+  const uint32_t grid = ncol * (cdiv(N, BM) + (uint32_t)E + 1);
+  hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, false>), dim3(grid),
+                     dim3(256), 0, st, (const S*)act, (const S*)wd,
+                     (const S*)wd, (S*)y, offsets, N, (int)I, (int)H, E,
+                     ncol, E + 1);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_generic_pair(const void* xd, int64_t N, int64_t H,
+                               int64_t I, int E, const void* wg,
+                               const void* wu, const void* wd,
+                               const uint32_t* offsets, void* act, void* y,
+                               hipStream_t st) {
+  using S = typename Storage<D>::T;
+  {
+    const uint32_t ncol = cdiv(I, 32);
+    const uint32_t grid = ncol * (cdiv(N, 64) + (uint32_t)E);
+    hipLaunchKernelGGL((gemm_generic_kernel<D, true>), dim3(grid), dim3(256),
+                       0, st, (const S*)xd, (const S*)wg, (const S*)wu,
+                       (S*)act, offsets, N, (int)H, (int)I, E, ncol, E);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  timing_mark(5, st);
+  const uint32_t ncol = cdiv(H, 64);
+  const uint32_t grid = ncol * (cdiv(N, 64) + (uint32_t)E + 1);
+  hipLaunchKernelGGL((gemm_generic_kernel<D, false>), dim3(grid), dim3(256),
+                     0, st, (const S*)act, (const S*)wd, (const S*)wd,
+                     (S*)y, offsets, N, (int)I, (int)H, E, ncol, E + 1);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
+                          int E, const void* wg, const void* wu,
+                          const void* wd, const uint32_t* offsets, void* act,
+                          void* y, hipStream_t st) {
+  // Few rows per expert (decode): short row blocks waste less work.
+  if (N < 96 * (int64_t)E)
+    return launch_mfma_pair<D, 32, 128, 1>(xd, N, H, I, E, wg, wu, wd,
+                                           offsets, act, y, st);
+  return launch_mfma_pair<D, 128, 128, 2>(xd, N, H, I, E, wg, wu, wd,
+                                          offsets, act, y, st);
+}
+
+}  // namespace
+
+hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
+                          int64_t I, int E, const void* w_gate,
+                          const void* w_up, const void* w_down,
+                          const uint32_t* offsets, void* act, void* y,
+                          hipStream_t st) {
+  const uintptr_t al = (uintptr_t)xd | (uintptr_t)w_gate | (uintptr_t)w_up |
+                       (uintptr_t)w_down | (uintptr_t)act | (uintptr_t)y;
+  const bool mfma = dt != DT_F32 && H % 8 == 0 && I % 8 == 0 && al % 16 == 0;
+  if (mfma) {
+    if (dt == DT_BF16)
+      return launch_mfma_dt<DT_BF16>(xd, N, H, I, E, w_gate, w_up, w_down,
+                                     offsets, act, y, st);
+    return launch_mfma_dt<DT_F16>(xd, N, H, I, E, w_gate, w_up, w_down,
+                                  offsets, act, y, st);
+  }
+  switch (dt) {
+    case DT_F32:
+      return launch_generic_pair<DT_F32>(xd, N, H, I, E, w_gate, w_up, w_down,
+                                         offsets, act, y, st);
+    case DT_F16:
+      return launch_generic_pair<DT_F16>(xd, N, H, I, E, w_gate, w_up, w_down,
+                                         offsets, act, y, st);
+    default:
+      return launch_generic_pair<DT_BF16>(xd, N, H, I, E, w_gate, w_up,
+                                          w_down, offsets, act, y, st);
+  }
+}
+
+}  // namespace moe

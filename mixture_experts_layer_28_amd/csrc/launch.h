@@ -1,0 +1,52 @@
+// Internal launchers of the libmoe kernels.  Host code only calls these after
+// every argument has been validated; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- instrumentation -------------------------------------------------------
+// Records the n-th timing mark on `st` if the caller installed events
+// (moe_set_timing_events); a no-op otherwise.
+void timing_mark(int n, hipStream_t st);
+
+// ---- routing ---------------------------------------------------------------
+hipError_t launch_route(const void* logits, int ldt, int64_t T, int E, int k,
+                        int renorm, uint32_t* idx, void* w, hipStream_t st);
+
+// ---- dispatch --------------------------------------------------------------
+// Scratch layout: a table of per-chunk expert counts [nchunks][E+1] u32,
+// reused in place for the per-chunk row bases.
+struct DispatchPlan {
+  int64_t N;        // T * k entries
+  int64_t chunk;    // entries per chunk (multiple of 64)
+  int64_t nchunks;  // ceil(N / chunk)
+  int waves;        // chunks (waves) per count workgroup
+  size_t table_bytes;
+};
+DispatchPlan plan_dispatch(int64_t T, int64_t E, int64_t k);
+
+hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,
+                           int E, int k, const uint32_t* idx, void* xd,
+                           uint32_t* offsets, uint32_t* row_expert,
+                           uint32_t* row_token, uint32_t* token_row,
+                           void* workspace, const DispatchPlan& plan,
+                           hipStream_t st);
+
+// ---- experts ---------------------------------------------------------------
+hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
+                          int64_t I, int E, const void* w_gate,
+                          const void* w_up, const void* w_down,
+                          const uint32_t* offsets, void* act, void* y,
+                          hipStream_t st);
+
+// ---- combine ---------------------------------------------------------------
+hipError_t launch_combine(const void* y, int dt, int64_t N, int64_t T,
+                          int64_t H, int k, const void* w, int wdt,
+                          const uint32_t* token_row, void* out,
+                          hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,340 @@
+// C ABI of libmoe: argument checks, workspace arithmetic and launch order.
+//
+// Every check below runs on the host before anything is enqueued and never
+// reads device memory.  The API mirrors the staged and one-call forms of the
+// ruDNN MoE interface (ruDNN user guide, section 6 "calling MoE"; experts page
+// SwiGluExperts::new / forward_dispatched_with_strategy / forward), whose
+// MoeError results become status codes here.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_marks[MOE_TIMING_EVENTS];
+thread_local int g_nmarks = 0;
+thread_local bool g_in_forward = false;
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return MOE_OK;
+}
+
+int hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_F16 || d == MOE_BF16; }
+int64_t dsize(int d) { return d == MOE_F32 ? 4 : 2; }
+
+// a * b without int64 overflow (both >= 0)
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+bool bytes_ok(int64_t a, int64_t b, int64_t s) {
+  int64_t t;
+  return mul_ok(a, b, &t) && mul_ok(t, s, &t);
+}
+
+constexpr int64_t kMaxRows = 0xffffffffLL;  // row ids are uint32
+constexpr int64_t kMaxRouteE = 65536;
+constexpr int64_t kMaxDispatchE = 16383;    // count table fits LDS
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+int check_route(const void* logits, int ldt, int64_t T, int64_t E,
+                int64_t k, const void* idx, const void* w) {
+  if (!valid_dtype(ldt)) return fail(MOE_ERR_DTYPE, "moe_route: unknown logits dtype %d", ldt);
+  if (T < 0) return fail(MOE_ERR_SHAPE, "moe_route: T must be >= 0");
+  if (E < 1) return fail(MOE_ERR_SHAPE, "moe_route: E must be >= 1");
+  if (E > kMaxRouteE) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E > %lld", (long long)kMaxRouteE);
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "moe_route: top_k must satisfy 1 <= top_k <= E");
+  int64_t n;
+  if (!mul_ok(T, k, &n) || n > kMaxRows) return fail(MOE_ERR_SHAPE, "moe_route: T*top_k must be < 2^32");
+  if (!bytes_ok(T, E, 4)) return fail(MOE_ERR_SHAPE, "moe_route: T*E overflows");
+  if (T > 0 && (!logits || !idx || !w)) return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+  return MOE_OK;
+}
+
+int check_dispatch(const void* x, int dt, int64_t T, int64_t H, int64_t E,
+                   int64_t k, const void* idx, const void* xd,
+                   const void* offsets, const void* row_expert,
+                   const void* row_token, const void* token_row) {
+  if (!valid_dtype(dt)) return fail(MOE_ERR_DTYPE, "moe_dispatch: unknown dtype %d", dt);
+  if (T < 0) return fail(MOE_ERR_SHAPE, "moe_dispatch: T must be >= 0");
+  if (H < 1) return fail(MOE_ERR_SHAPE, "moe_dispatch: H must be >= 1");
+  if (E < 1) return fail(MOE_ERR_SHAPE, "moe_dispatch: E must be >= 1");
+  if (E > kMaxDispatchE) return fail(MOE_ERR_UNSUPPORTED, "moe_dispatch: E > %lld", (long long)kMaxDispatchE);
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: top_k must satisfy 1 <= top_k <= E");
+  int64_t n;
+  if (!mul_ok(T, k, &n) || n > kMaxRows) return fail(MOE_ERR_SHAPE, "moe_dispatch: T*top_k must be < 2^32");
+  if (!bytes_ok(n, H, dsize(dt))) return fail(MOE_ERR_SHAPE, "moe_dispatch: N*H overflows");
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: null offsets");
+  if (T > 0 && (!x || !idx || !xd || !row_expert || !row_token || !token_row))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: null pointer");
+  return MOE_OK;
+}
+
+int check_experts(const void* xd, int dt, int64_t N, int64_t H, int64_t I,
+                  int64_t E, const void* wg, const void* wu, const void* wd,
+                  const void* offsets, const void* act, const void* y) {
+  if (!valid_dtype(dt)) return fail(MOE_ERR_DTYPE, "moe_experts_forward: unknown dtype %d", dt);
+  if (N < 0) return fail(MOE_ERR_SHAPE, "moe_experts_forward: N must be >= 0");
+  if (N > kMaxRows) return fail(MOE_ERR_SHAPE, "moe_experts_forward: N must be < 2^32");
+  if (E < 1 || H < 1 || I < 1) return fail(MOE_ERR_SHAPE, "moe_experts_forward: E, H and I must be >= 1");
+  if (H > INT32_MAX || I > INT32_MAX || E > kMaxDispatchE)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_experts_forward: H, I < 2^31 and E <= %lld required", (long long)kMaxDispatchE);
+  int64_t ei;
+  if (!mul_ok(E, I, &ei) || !bytes_ok(ei, H, dsize(dt)))
+    return fail(MOE_ERR_SHAPE, "moe_experts_forward: weight size overflows");
+  if (!bytes_ok(N, H > I ? H : I, dsize(dt))) return fail(MOE_ERR_SHAPE, "moe_experts_forward: N*max(H,I) overflows");
+  if (!wg || !wu || !wd) return fail(MOE_ERR_INVALID_ARG, "moe_experts_forward: null weight pointer");
+  if (N > 0 && (!xd || !act || !y || !offsets)) return fail(MOE_ERR_INVALID_ARG, "moe_experts_forward: null pointer");
+  return MOE_OK;
+}
+
+int check_combine(const void* y, int dt, int64_t N, int64_t T, int64_t H,
+                  int64_t k, const void* w, int wdt, const void* token_row,
+                  const void* out) {
+  if (!valid_dtype(dt) || !valid_dtype(wdt)) return fail(MOE_ERR_DTYPE, "moe_combine: unknown dtype");
+  if (T < 0 || N < 0 || H < 1) return fail(MOE_ERR_SHAPE, "moe_combine: T, N >= 0 and H >= 1 required");
+  if (k < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine: top_k must be >= 1");
+  int64_t n;
+  if (!mul_ok(T, k, &n) || n > kMaxRows || N > kMaxRows) return fail(MOE_ERR_SHAPE, "moe_combine: T*top_k and N must be < 2^32");
+  if (!bytes_ok(N > T ? N : T, H, dsize(dt))) return fail(MOE_ERR_SHAPE, "moe_combine: size overflows");
+  if (k > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: top_k > 1024");
+  if (T > 0 && (!y || !w || !token_row || !out)) return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
+  return MOE_OK;
+}
+
+struct ForwardLayout {
+  size_t idx, w, offsets, row_expert, row_token, token_row, xd, dws, act, y,
+      total;
+};
+
+ForwardLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E,
+                             int64_t k, int dt, int ldt) {
+  ForwardLayout L;
+  const int64_t N = T * k;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at = align_up(at + bytes);
+    return here;
+  };
+  L.idx = take((size_t)N * 4);
+  L.w = take((size_t)N * dsize(ldt));
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.row_expert = take((size_t)N * 4);
+  L.row_token = take((size_t)N * 4);
+  L.token_row = take((size_t)N * 4);
+  L.xd = take((size_t)N * H * dsize(dt));
+  L.dws = take(moe::plan_dispatch(T, E, k).table_bytes);
+  L.act = take((size_t)N * I * dsize(dt));
+  L.y = take((size_t)N * H * dsize(dt));
+  L.total = at;
+  return L;
+}
+
+}  // namespace
+
+namespace moe {
+void timing_mark(int n, hipStream_t st) {
+  if (g_in_forward && g_nmarks == MOE_TIMING_EVENTS && n >= 0 && n < g_nmarks)
+    (void)hipEventRecord(g_marks[n], st);
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_set_timing_events(void* const* events, int count) {
+  if (count == 0) {
+    g_nmarks = 0;
+    return ok();
+  }
+  if (count != MOE_TIMING_EVENTS || !events)
+    return fail(MOE_ERR_INVALID_ARG, "moe_set_timing_events: need %d events", MOE_TIMING_EVENTS);
+  for (int i = 0; i < count; ++i) {
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "moe_set_timing_events: null event");
+    g_marks[i] = (hipEvent_t)events[i];
+  }
+  g_nmarks = count;
+  return ok();
+}
+
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_SHAPE: return "invalid or overflowing shape";
+    case MOE_ERR_DTYPE: return "unknown dtype";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+int moe_route(const void* logits, int ldt, int64_t T, int64_t E,
+              int64_t top_k, int renormalize, uint32_t* idx, void* weights,
+              void* stream) {
+  const int s = check_route(logits, ldt, T, E, top_k, idx, weights);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  return hip_status(moe::launch_route(logits, ldt, T, (int)E, (int)top_k,
+                                      renormalize ? 1 : 0, idx, weights,
+                                      (hipStream_t)stream),
+                    "moe_route");
+}
+
+size_t moe_dispatch_workspace_size(int64_t T, int64_t E, int64_t top_k) {
+  int64_t n;
+  if (T < 0 || E < 1 || E > kMaxDispatchE || top_k < 1 || top_k > E ||
+      !mul_ok(T, top_k, &n) || n > kMaxRows)
+    return 0;
+  return align_up(moe::plan_dispatch(T, E, top_k).table_bytes) + 256;
+}
+
+int moe_dispatch(const void* x, int dt, int64_t T, int64_t H, int64_t E,
+                 int64_t top_k, const uint32_t* idx, void* xd,
+                 uint32_t* offsets, uint32_t* row_expert, uint32_t* row_token,
+                 uint32_t* token_row, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int s = check_dispatch(x, dt, T, H, E, top_k, idx, xd, offsets, row_expert,
+                         row_token, token_row);
+  if (s != MOE_OK) return s;
+  const size_t need = moe_dispatch_workspace_size(T, E, top_k);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: workspace needs %zu bytes", need);
+  if ((uintptr_t)workspace % 4 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: workspace must be 4-byte aligned");
+  const moe::DispatchPlan plan = moe::plan_dispatch(T, E, top_k);
+  // T == 0 still writes offsets (all zero): every segment is empty.
+  return hip_status(
+      moe::launch_dispatch(x, dt, T, H, (int)E, (int)top_k, idx, xd, offsets,
+                           row_expert, row_token, token_row, workspace, plan,
+                           (hipStream_t)stream),
+      "moe_dispatch");
+}
+
+int moe_experts_forward(const void* xd, int dt, int64_t N, int64_t H,
+                        int64_t I, int64_t E, const void* w_gate,
+                        const void* w_up, const void* w_down,
+                        const uint32_t* offsets, void* act, void* y,
+                        void* stream) {
+  const int s = check_experts(xd, dt, N, H, I, E, w_gate, w_up, w_down,
+                              offsets, act, y);
+  if (s != MOE_OK) return s;
+  if (N == 0) return ok();
+  return hip_status(moe::launch_experts(xd, dt, N, H, I, (int)E, w_gate, w_up,
+                                        w_down, offsets, act, y,
+                                        (hipStream_t)stream),
+                    "moe_experts_forward");
+}
+
+int moe_combine(const void* y, int dt, int64_t N, int64_t T, int64_t H,
+                int64_t top_k, const void* weights, int wdt,
+                const uint32_t* token_row, void* out, void* stream) {
+  const int s = check_combine(y, dt, N, T, H, top_k, weights, wdt, token_row,
+                              out);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  return hip_status(moe::launch_combine(y, dt, N, T, H, (int)top_k, weights,
+                                        wdt, token_row, out,
+                                        (hipStream_t)stream),
+                    "moe_combine");
+}
+
+size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E,
+                                  int64_t top_k, int dt, int ldt) {
+  if (!valid_dtype(dt) || !valid_dtype(ldt) || T < 0 || H < 1 || I < 1 ||
+      E < 1 || E > kMaxDispatchE || top_k < 1 || top_k > E)
+    return 0;
+  int64_t n;
+  if (!mul_ok(T, top_k, &n) || n > kMaxRows ||
+      !bytes_ok(n, H > I ? H : I, 16))
+    return 0;
+  return forward_layout(T, H, I, E, top_k, dt, ldt).total;
+}
+
+int moe_forward(const void* x, int dt, const void* logits, int ldt,
+                int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                int renormalize, const void* w_gate, const void* w_up,
+                const void* w_down, void* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int s = check_route(logits, ldt, T, E, top_k, workspace, workspace);
+  if (s != MOE_OK) return s;
+  // x stands in for the workspace-resident offsets/act/y buffers here;
+  // the workspace itself is checked below.
+  s = check_experts(x, dt, T * top_k, H, I, E, w_gate, w_up, w_down, x, x, x);
+  if (s != MOE_OK) return s;
+  if (T > 0 && (!x || !out)) return fail(MOE_ERR_INVALID_ARG, "moe_forward: null pointer");
+  const size_t need = moe_forward_workspace_size(T, H, I, E, top_k, dt, ldt);
+  if (need == 0) return fail(MOE_ERR_SHAPE, "moe_forward: sizes out of range");
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward: workspace needs %zu bytes", need);
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward: workspace must be 256-byte aligned");
+  if (T == 0) return ok();
+
+  const ForwardLayout L = forward_layout(T, H, I, E, top_k, dt, ldt);
+  char* ws = (char*)workspace;
+  uint32_t* idx = (uint32_t*)(ws + L.idx);
+  void* w = ws + L.w;
+  uint32_t* offsets = (uint32_t*)(ws + L.offsets);
+  uint32_t* row_expert = (uint32_t*)(ws + L.row_expert);
+  uint32_t* row_token = (uint32_t*)(ws + L.row_token);
+  uint32_t* token_row = (uint32_t*)(ws + L.token_row);
+  void* xd = ws + L.xd;
+  void* dws = ws + L.dws;
+  void* act = ws + L.act;
+  void* y = ws + L.y;
+  const int64_t N = T * top_k;
+  const hipStream_t st = (hipStream_t)stream;
+
+  struct Marking {
+    Marking() { g_in_forward = true; }
+    ~Marking() { g_in_forward = false; }
+  } marking;
+  moe::timing_mark(0, st);
+  hipError_t err = moe::launch_route(logits, ldt, T, (int)E, (int)top_k,
+                                     renormalize ? 1 : 0, idx, w, st);
+  if (err != hipSuccess) return hip_status(err, "moe_forward(route)");
+  moe::timing_mark(1, st);
+  err = moe::launch_dispatch(x, dt, T, H, (int)E, (int)top_k, idx, xd,
+                             offsets, row_expert, row_token, token_row, dws,
+                             moe::plan_dispatch(T, E, top_k), st);
+  if (err != hipSuccess) return hip_status(err, "moe_forward(dispatch)");
+  moe::timing_mark(4, st);
+  err = moe::launch_experts(xd, dt, N, H, I, (int)E, w_gate, w_up, w_down,
+                            offsets, act, y, st);
+  if (err != hipSuccess) return hip_status(err, "moe_forward(experts)");
+  moe::timing_mark(6, st);
+  err = moe::launch_combine(y, dt, N, T, H, (int)top_k, w, ldt, token_row,
+                            out, st);
+  moe::timing_mark(7, st);
+  return hip_status(err, "moe_forward(combine)");
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+"""Thin torch binding of libmoe: one function per C entry point, same names.
+
+Argument marshalling only: tensors are checked for device, dtype and shape,
+made contiguous, outputs are allocated with torch (device memory), and the
+current torch stream is passed down.  Every step of the computation runs in
+the HIP kernels of libmoe.so.
+
+Index arrays that the C ABI types as uint32 are int32 tensors here (same
+bits; every value stays below 2**31 at the sizes torch can allocate).
+"""
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F16, MOE_F32, check, lib
+
+_DT = {torch.float32: MOE_F32, torch.float16: MOE_F16,
+       torch.bfloat16: MOE_BF16}
+_U32 = torch.int32
+
+
+def _dt(t, what):
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError("%s: dtype %s is not F32, F16 or BF16" % (what, t.dtype))
+
+
+def _dev(*ts):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("libmoe tensors must be on a HIP device, got %s" % dev)
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _c(t):
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def _p(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def moe_route(logits, top_k, renormalize=True, idx=None, weights=None):
+    """Softmax/top-k routing.  logits [T,E] -> (idx int32 [T,k],
+    weights [T,k] in the logits dtype)."""
+    logits = _c(logits)
+    dev = _dev(logits)
+    T, E = logits.shape
+    if idx is None:
+        idx = torch.empty((T, top_k), dtype=_U32, device=dev)
+    if weights is None:
+        weights = torch.empty((T, top_k), dtype=logits.dtype, device=dev)
+    check(lib().moe_route(_p(logits), _dt(logits, "logits"), T, E, top_k,
+                          int(bool(renormalize)), _p(idx), _p(weights),
+                          _stream(dev)))
+    return idx, weights
+
+
+def moe_dispatch_workspace_size(T, E, top_k):
+    return lib().moe_dispatch_workspace_size(T, E, top_k)
+
+
+def moe_dispatch(x, idx, num_experts, workspace=None):
+    """Compact dispatch.  x [T,H], idx [T,k] -> dict of xd [N,H],
+    offsets [E+1], row_expert [N], row_token [N], token_row [T,k]."""
+    x = _c(x)
+    idx = _c(idx)
+    dev = _dev(x, idx)
+    T, H = x.shape
+    k = idx.shape[1]
+    if idx.shape[0] != T:
+        raise ValueError("idx must be [T, top_k]")
+    N = T * k
+    ws_bytes = moe_dispatch_workspace_size(T, num_experts, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = dict(
+        xd=torch.empty((N, H), dtype=x.dtype, device=dev),
+        offsets=torch.empty(num_experts + 1, dtype=_U32, device=dev),
+        row_expert=torch.empty(N, dtype=_U32, device=dev),
+        row_token=torch.empty(N, dtype=_U32, device=dev),
+        token_row=torch.empty((T, k), dtype=_U32, device=dev),
+    )
+    check(lib().moe_dispatch(
+        _p(x), _dt(x, "x"), T, H, num_experts, k, _p(idx), _p(out["xd"]),
+        _p(out["offsets"]), _p(out["row_expert"]), _p(out["row_token"]),
+        _p(out["token_row"]), _p(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def moe_experts_forward(xd, offsets, w_gate, w_up, w_down, act=None, y=None):
+    """SwiGLU experts over segments.  Returns y [N,H] (act [N,I] is the
+    intermediate buffer; pass one in to keep it)."""
+    xd, offsets = _c(xd), _c(offsets)
+    w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
+    dev = _dev(xd, offsets, w_gate, w_up, w_down)
+    N, H = xd.shape
+    E, I, H2 = w_gate.shape
+    if H2 != H or tuple(w_up.shape) != (E, I, H) or tuple(
+            w_down.shape) != (E, H, I):
+        raise ValueError("expert weight shapes must be gate/up [E,I,H], "
+                         "down [E,H,I] with H matching xd")
+    for w in (w_gate, w_up, w_down):
+        if w.dtype != xd.dtype:
+            raise TypeError("expert weights and rows must share one dtype")
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must have E+1 entries")
+    if act is None:
+        act = torch.empty((N, I), dtype=xd.dtype, device=dev)
+    if y is None:
+        y = torch.empty((N, H), dtype=xd.dtype, device=dev)
+    check(lib().moe_experts_forward(
+        _p(xd), _dt(xd, "xd"), N, H, I, E, _p(w_gate), _p(w_up), _p(w_down),
+        _p(offsets), _p(act), _p(y), _stream(dev)))
+    return y
+
+
+def moe_combine(y, weights, token_row, out=None):
+    """Weighted merge.  y [N,H], weights [T,k], token_row [T,k] ->
+    out [T,H]."""
+    y, weights, token_row = _c(y), _c(weights), _c(token_row)
+    dev = _dev(y, weights, token_row)
+    N, H = y.shape
+    T, k = weights.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=y.dtype, device=dev)
+    check(lib().moe_combine(_p(y), _dt(y, "y"), N, T, H, k, _p(weights),
+                            _dt(weights, "weights"), _p(token_row), _p(out),
+                            _stream(dev)))
+    return out
+
+
+def moe_forward_workspace_size(T, H, I, E, top_k, dtype, logits_dtype=None):
+    ldt = _DT[logits_dtype if logits_dtype is not None else dtype]
+    return lib().moe_forward_workspace_size(T, H, I, E, top_k, _DT[dtype], ldt)
+
+
+def moe_forward(x, logits, w_gate, w_up, w_down, top_k, renormalize=True,
+                out=None, workspace=None):
+    """Whole forward: route -> dispatch -> experts -> combine, one call."""
+    x, logits = _c(x), _c(logits)
+    w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
+    dev = _dev(x, logits, w_gate, w_up, w_down)
+    T, H = x.shape
+    E, I, _ = w_gate.shape
+    if logits.shape != (T, E):
+        raise ValueError("logits must be [T, E]")
+    ws = moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    check(lib().moe_forward(
+        _p(x), _dt(x, "x"), _p(logits), _dt(logits, "logits"), T, H, I, E,
+        top_k, int(bool(renormalize)), _p(w_gate), _p(w_up), _p(w_down),
+        _p(out), _p(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+__all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
+           "moe_experts_forward", "moe_combine", "moe_forward",
+           "moe_forward_workspace_size", "_lib"]

@@ -1,0 +1,136 @@
+"""The C ABI on a host without a GPU: libmoe.so loads, exports every entry
+point include/moe.h declares, and rejects bad arguments before enqueueing
+anything (no device pointer is touched, so dummy addresses are safe)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_28_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "moe.h")
+FAKE = 0x1000  # never dereferenced: every call below fails validation
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_symbol():
+    L = _lib.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code in range(6):
+        assert L.moe_status_string(code)
+    assert L.moe_status_string(99) == b"unknown status"
+
+
+def _last():
+    return _lib.lib().moe_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 0, 4, 8, 0, 1, FAKE, FAKE, None), 1),     # top_k = 0
+    ((FAKE, 0, 4, 8, 9, 1, FAKE, FAKE, None), 1),     # top_k > E
+    ((FAKE, 7, 4, 8, 2, 1, FAKE, FAKE, None), 3),     # bad dtype
+    ((FAKE, 0, -1, 8, 2, 1, FAKE, FAKE, None), 2),    # T < 0
+    ((FAKE, 0, 4, 0, 1, 1, FAKE, FAKE, None), 2),     # E = 0
+    ((None, 0, 4, 8, 2, 1, FAKE, FAKE, None), 1),     # null logits
+    ((FAKE, 0, 4, 70000, 2, 1, FAKE, FAKE, None), 4),  # E too large
+    ((FAKE, 0, 1 << 31, 8, 2, 1, FAKE, FAKE, None), 2),  # T*k >= 2^32
+])
+def test_route_rejects(args, status):
+    assert _lib.lib().moe_route(*args) == status
+    assert _last()
+
+
+def test_route_empty_is_ok_without_device():
+    assert _lib.lib().moe_route(None, 2, 0, 8, 2, 1, None, None, None) == 0
+    assert _last() == ""
+
+
+def test_dispatch_rejects():
+    L = _lib.lib()
+    ws = L.moe_dispatch_workspace_size(10, 4, 2)
+    assert ws > 0
+    args = [FAKE, 2, 10, 16, 4, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            ws, None]
+    bad = list(args)
+    bad[13] = ws - 1  # workspace too small
+    assert L.moe_dispatch(*bad) == 1 and "workspace" in _last()
+    bad = list(args)
+    bad[5] = 5  # top_k > E
+    assert L.moe_dispatch(*bad) == 1
+    bad = list(args)
+    bad[4] = 20000  # E beyond the dispatch limit
+    assert L.moe_dispatch(*bad) == 4
+    bad = list(args)
+    bad[8] = None  # offsets
+    assert L.moe_dispatch(*bad) == 1
+    bad = list(args)
+    bad[12] = FAKE + 2  # misaligned workspace
+    assert L.moe_dispatch(*bad) == 1
+
+
+def test_experts_rejects():
+    L = _lib.lib()
+    base = [FAKE, 2, 100, 64, 32, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    for i, v, st in [(1, 9, 3), (2, -1, 2), (3, 0, 2), (4, 0, 2), (5, 0, 2),
+                     (6, None, 1), (9, None, 1), (0, None, 1), (11, None, 1),
+                     (2, 1 << 33, 2),
+                     (3, 1 << 40, 4)]:
+        a = list(base)
+        a[i] = v
+        assert L.moe_experts_forward(*a) == st, (i, v)
+    a = list(base)
+    a[2] = 0  # N = 0: nothing to do, valid
+    a[0] = a[9] = a[10] = a[11] = None
+    assert L.moe_experts_forward(*a) == 0
+
+
+def test_combine_rejects():
+    L = _lib.lib()
+    base = [FAKE, 2, 20, 10, 16, 2, FAKE, 2, FAKE, FAKE, None]
+    for i, v, st in [(1, 5, 3), (7, 5, 3), (5, 0, 1), (4, 0, 2),
+                     (8, None, 1), (5, 2000, 4)]:
+        a = list(base)
+        a[i] = v
+        assert L.moe_combine(*a) == st, (i, v)
+
+
+def test_forward_workspace_and_rejects():
+    L = _lib.lib()
+    ws = L.moe_forward_workspace_size(64, 128, 256, 8, 2, 0, 0)
+    N = 128
+    # every buffer is accounted for (each 256-byte aligned)
+    need = N * 4 + N * 4 + 9 * 4 + 3 * N * 4 + N * 128 * 4 + N * 256 * 4 \
+        + N * 128 * 4
+    assert ws >= need and ws % 256 == 0
+    assert L.moe_forward_workspace_size(64, 128, 256, 8, 9, 0, 0) == 0
+    args = [FAKE, 0, FAKE, 0, 64, 128, 256, 8, 2, 1, FAKE, FAKE, FAKE, FAKE,
+            0x10000, ws, None]
+    a = list(args)
+    a[15] = ws - 1
+    assert L.moe_forward(*a) == 1 and "workspace" in _last()
+    a = list(args)
+    a[14] = 0x10010  # not 256-byte aligned
+    assert L.moe_forward(*a) == 1
+    a = list(args)
+    a[8] = 0
+    assert L.moe_forward(*a) == 1
+    a = list(args)
+    a[10] = None
+    assert L.moe_forward(*a) == 1
