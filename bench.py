@@ -37,7 +37,8 @@ WORKLOADS = {
     "decode32": ("decode", 32),
     "decode256": ("decode", 256),
 }
-CPU_SAMPLE_TOKENS = {"mixtral": 3, "fine": 3, "decode32": 6, "decode256": 6}
+CPU_SAMPLE_MAX_TOKENS = 256
+CPU_SAMPLE_SECONDS = 15.0
 
 
 def parse():
@@ -74,8 +75,10 @@ def algorithmic(wl, counts):
     }
 
 
-def cpu_baseline(wl, name, tokens):
-    """The oracle, untuned, on a bounded sample of the workload's tokens."""
+def cpu_baseline(wl):
+    """The oracle, untuned, on a bounded sample of the workload's tokens:
+    tokens drawn at random are pushed through the oracle one at a time
+    until about CPU_SAMPLE_SECONDS have passed."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -86,10 +89,16 @@ def cpu_baseline(wl, name, tokens):
     host = {key: workloads.to_numpy(wl[key], fmt)
             for key in ("x", "logits", "w_gate", "w_up", "w_down")}
     rng = np.random.default_rng(123)
-    sample = sorted(rng.choice(wl["T"], size=tokens, replace=False).tolist())
+    order = rng.permutation(wl["T"])[:CPU_SAMPLE_MAX_TOKENS].tolist()
+    tokens = 0
     t0 = time.perf_counter()
-    forward_tokens(host["x"], host["logits"], host["w_gate"], host["w_up"],
-                   host["w_down"], wl["k"], wl["renorm"], fmt, sample)
+    for t in order:
+        forward_tokens(host["x"], host["logits"], host["w_gate"],
+                       host["w_up"], host["w_down"], wl["k"], wl["renorm"],
+                       fmt, [t])
+        tokens += 1
+        if time.perf_counter() - t0 >= CPU_SAMPLE_SECONDS:
+            break
     dt = time.perf_counter() - t0
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads,
@@ -192,7 +201,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.workload, CPU_SAMPLE_TOKENS[args.workload])
+        cpu = cpu_baseline(wl)
 
     line = {
         "metric": "MoE forward tokens/sec",
