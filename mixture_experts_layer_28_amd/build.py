@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["moe_abi.cpp", "route.hip", "dispatch.hip", "gemm.hip",
-           "combine.hip"]
+           "gemm_big.hip", "combine.hip"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature",
                 "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
@@ -49,6 +49,10 @@ def build(verbose=True):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    # every symbol must resolve: a kernel whose host stub went missing
+    # shows up here rather than at the first call
+    import ctypes
+    ctypes.CDLL(tmp)
     os.replace(tmp, OUT)
     if verbose:
         print("built", OUT)

@@ -43,6 +43,19 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// Values every lane of a wavefront agrees on (e.g. read back from LDS) held
+// in scalar registers: the compiler cannot prove such loads uniform, and a
+// buffer descriptor built from a "divergent" value forces a loop over lanes
+// around every buffer instruction.
+__device__ __forceinline__ int uniform(int v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Logical workgroup id that keeps consecutive ids on one XCD.  The
 // dispatcher deals workgroups to the 8 XCDs of an MI355X round-robin, so
 // hardware id b runs on XCD b % 8; this renumbers so XCD x owns the

@@ -35,81 +35,12 @@
 // A segment s = E (rows [offsets[E], N), produced by out-of-range expert
 // ids) is written as zeros by the down launch.
 
-#include "device_common.h"
-#include "launch.h"
+#include <cstdlib>
+
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
-
-struct TileInfo {
-  int64_t lo, hi, row0;
-  int e, col, found;
-};
-
-// Executed by the 64 lanes of wavefront 0.  Segment s < E is
-// [offsets[s], offsets[s+1]); segment E (only if nseg > E) is
-// [offsets[E], N).  Bounds are clamped into [0, N] and made monotone so
-// that any offsets array keeps every access in bounds.
-__device__ void locate_tile(uint32_t L, const uint32_t* __restrict__ offsets,
-                            int E, int64_t N, int BM, uint32_t ncol, int nseg,
-                            TileInfo* ti) {
-  const int lane = threadIdx.x;
-  if (lane == 0) ti->found = 0;
-  uint32_t base = 0;
-  for (int s0 = 0; s0 < nseg; s0 += 64) {
-    const int s = s0 + lane;
-    int64_t lo = 0, hi = 0;
-    if (s < nseg) {
-      lo = offsets[s];
-      lo = lo < N ? lo : N;
-      hi = s < E ? (int64_t)offsets[s + 1] : N;
-      hi = hi < lo ? lo : (hi > N ? N : hi);
-    }
-    const uint32_t nt = (uint32_t)((hi - lo + BM - 1) / BM);
-    const uint32_t cnt = nt * ncol;
-    uint32_t inc = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += t;
-    }
-    const uint32_t exc = inc - cnt;
-    const bool hit = L >= base + exc && L < base + inc;
-    if (__ballot(hit)) {
-      if (hit) {
-        const uint32_t local = L - base - exc;
-        ti->e = s;
-        ti->lo = lo;
-        ti->hi = hi;
-        ti->col = (int)(local / nt);
-        ti->row0 = lo + (int64_t)(local % nt) * BM;
-        ti->found = 1;
-      }
-      return;
-    }
-    base += __shfl(inc, 63, 64);
-  }
-}
-
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-template <int D> struct Frag;
-template <> struct Frag<DT_BF16> {
-  using V = bf16x8;
-  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Frag<DT_F16> {
-  using V = f16x8;
-  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
-}
 
 template <int D, int BM, int BN, int WGM, bool GATEUP>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
@@ -138,9 +69,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   if (tid < 64) locate_tile(L, offsets, E, N, BM, ncol, nseg, &ti);
   __syncthreads();
   if (!ti.found) return;
-  const int e = ti.e;
-  const int64_t hi = ti.hi, row0 = ti.row0;
-  const int64_t n0 = (int64_t)ti.col * TCOLS;
+  const int e = uniform(ti.e);
+  const int64_t hi = uniform(ti.hi), row0 = uniform(ti.row0);
+  const int64_t n0 = (int64_t)uniform(ti.col) * TCOLS;
 
   if (e >= E) {  // rows of out-of-range experts: zeros
     for (int q = tid; q < BM * TCOLS; q += 256) {
@@ -296,9 +227,9 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
   if (tid < 64) locate_tile(L, offsets, E, N, BM, ncol, nseg, &ti);
   __syncthreads();
   if (!ti.found) return;
-  const int e = ti.e;
-  const int64_t hi = ti.hi, row0 = ti.row0;
-  const int64_t n0 = (int64_t)ti.col * TCOLS;
+  const int e = uniform(ti.e);
+  const int64_t hi = uniform(ti.hi), row0 = uniform(ti.row0);
+  const int64_t n0 = (int64_t)uniform(ti.col) * TCOLS;
   if (e >= E) {
     for (int q = tid; q < BM * TCOLS; q += 256) {
       const int64_t r = row0 + q / TCOLS, c = n0 + q % TCOLS;
@@ -379,8 +310,6 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
   }
 }
 
-inline uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
-
 template <int D, int BM, int BN, int WGM>
 hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                             int E, const void* wg, const void* wu,
@@ -441,6 +370,16 @@ hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
   if (N < 96 * (int64_t)E)
     return launch_mfma_pair<D, 32, 128, 1>(xd, N, H, I, E, wg, wu, wd,
                                            offsets, act, y, st);
+  // Prefill: 256 x 256 tiles when every buffer range fits 31 bits.
+  const int64_t lim = (int64_t)1 << 31;
+  if (H * I * 2 < lim && 256 * H * 2 < lim && 256 * I * 2 < lim) {
+    static const int variant = [] {
+      const char* v = getenv("MOE_GEMM_VARIANT");
+      return v ? atoi(v) : 2;
+    }();
+    return launch_experts_big(xd, D, N, H, I, E, wg, wu, wd, offsets, act, y,
+                              variant, st);
+  }
   return launch_mfma_pair<D, 128, 128, 2>(xd, N, H, I, E, wg, wu, wd,
                                           offsets, act, y, st);
 }

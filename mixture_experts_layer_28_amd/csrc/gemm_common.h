@@ -1,0 +1,115 @@
+// Device helpers shared by the grouped-GEMM kernels (gemm.hip,
+// gemm_big.hip): the device-side tile map, the LDS swizzle, the MFMA
+// fragment types and the SwiGLU epilogue.
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+struct TileInfo {
+  int64_t lo, hi, row0;
+  int e, col, found;
+};
+
+// Executed by the 64 lanes of wavefront 0.  Segment s < E is
+// [offsets[s], offsets[s+1]); segment E (only if nseg > E) is
+// [offsets[E], N).  Bounds are clamped into [0, N] and made monotone so
+// that any offsets array keeps every access in bounds.
+__device__ inline void locate_tile(uint32_t L, const uint32_t* __restrict__ offsets,
+                            int E, int64_t N, int BM, uint32_t ncol, int nseg,
+                            TileInfo* ti) {
+  const int lane = threadIdx.x;
+  if (lane == 0) ti->found = 0;
+  uint32_t base = 0;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    const int s = s0 + lane;
+    int64_t lo = 0, hi = 0;
+    if (s < nseg) {
+      lo = offsets[s];
+      lo = lo < N ? lo : N;
+      hi = s < E ? (int64_t)offsets[s + 1] : N;
+      hi = hi < lo ? lo : (hi > N ? N : hi);
+    }
+    const uint32_t nt = (uint32_t)((hi - lo + BM - 1) / BM);
+    const uint32_t cnt = nt * ncol;
+    uint32_t inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
+    }
+    const uint32_t exc = inc - cnt;
+    const bool hit = L >= base + exc && L < base + inc;
+    if (__ballot(hit)) {
+      if (hit) {
+        const uint32_t local = L - base - exc;
+        ti->e = s;
+        ti->lo = lo;
+        ti->hi = hi;
+        ti->col = (int)(local / nt);
+        ti->row0 = lo + (int64_t)(local % nt) * BM;
+        ti->found = 1;
+      }
+      return;
+    }
+    base += __shfl(inc, 63, 64);
+  }
+}
+
+// 16-byte chunk c of tile row r sits at chunk position c ^ swz(r) of the
+// row's 128 bytes.  Fragment reads take one chunk from 16 consecutive rows;
+// measured on gfx950, rotating by r & 7 spreads them as evenly as a
+// contiguous read.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
+
+template <int D> struct Frag;
+template <> struct Frag<DT_BF16> {
+  using V = bf16x8;
+  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Frag<DT_F16> {
+  using V = f16x8;
+  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+
+inline uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+// Raw buffer resource over [base, base + bytes): loads at offsets at or
+// beyond `bytes` return zeros (the hardware range check), which the GEMMs
+// use for K tails and for rows past a segment or a weight matrix.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                          uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)n, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i writes
+// lds + 16*i (gfx950 buffer_load_dwordx4 ... lds).  The LDS address space
+// cast exists on the device side only.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r,
+                                                  void* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void wait_vmem() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
+}  // namespace moe

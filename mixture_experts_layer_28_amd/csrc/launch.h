@@ -43,6 +43,15 @@ hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
                           const uint32_t* offsets, void* act, void* y,
                           hipStream_t st);
 
+// 256x256-tile kernels for prefill-sized segments (bf16/f16, H and I
+// multiples of 8, 16-byte aligned, every per-expert weight matrix and 256
+// rows of either operand under 2 GB).
+hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
+                              int64_t I, int E, const void* w_gate,
+                              const void* w_up, const void* w_down,
+                              const uint32_t* offsets, void* act, void* y,
+                              int variant, hipStream_t st);
+
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(const void* y, int dt, int64_t N, int64_t T,
                           int64_t H, int k, const void* w, int wdt,
