@@ -65,8 +65,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   __shared__ TileInfo ti;
 
   const int tid = threadIdx.x;
-  const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-  if (tid < 64) locate_tile(L, offsets, E, N, BM, ncol, nseg, &ti);
+  if (tid < 64)
+    locate_tile(blockIdx.x, gridDim.x, offsets, E, N, BM, ncol, nseg, &ti);
   __syncthreads();
   if (!ti.found) return;
   const int e = uniform(ti.e);
@@ -223,8 +223,8 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
   __shared__ float Bs[BK][BN + 1];
   __shared__ TileInfo ti;
   const int tid = threadIdx.x;
-  const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-  if (tid < 64) locate_tile(L, offsets, E, N, BM, ncol, nseg, &ti);
+  if (tid < 64)
+    locate_tile(blockIdx.x, gridDim.x, offsets, E, N, BM, ncol, nseg, &ti);
   __syncthreads();
   if (!ti.found) return;
   const int e = uniform(ti.e);
@@ -318,7 +318,7 @@ hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
   using S = typename Storage<D>::T;
   {
     const uint32_t ncol = cdiv(I, BN / 2);
-    const uint32_t grid = ncol * (cdiv(N, BM) + (uint32_t)E);
+    const uint32_t grid = tile_grid(ncol * (cdiv(N, BM) + (uint32_t)E));
     hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, true>), dim3(grid),
                        dim3(256), 0, st, (const S*)xd, (const S*)wg,
                        (const S*)wu, (S*)act, offsets, N, (int)H, (int)I, E,
@@ -328,7 +328,7 @@ hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
   }
   timing_mark(5, st);
   const uint32_t ncol = cdiv(H, BN);
-  const uint32_t grid = ncol * (cdiv(N, BM) + (uint32_t)E + 1);
+  const uint32_t grid = tile_grid(ncol * (cdiv(N, BM) + (uint32_t)E + 1));
   hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, false>), dim3(grid),
                      dim3(256), 0, st, (const S*)act, (const S*)wd,
                      (const S*)wd, (S*)y, offsets, N, (int)I, (int)H, E,
@@ -345,7 +345,7 @@ hipError_t launch_generic_pair(const void* xd, int64_t N, int64_t H,
   using S = typename Storage<D>::T;
   {
     const uint32_t ncol = cdiv(I, 32);
-    const uint32_t grid = ncol * (cdiv(N, 64) + (uint32_t)E);
+    const uint32_t grid = tile_grid(ncol * (cdiv(N, 64) + (uint32_t)E));
     hipLaunchKernelGGL((gemm_generic_kernel<D, true>), dim3(grid), dim3(256),
                        0, st, (const S*)xd, (const S*)wg, (const S*)wu,
                        (S*)act, offsets, N, (int)H, (int)I, E, ncol, E);
@@ -354,7 +354,7 @@ hipError_t launch_generic_pair(const void* xd, int64_t N, int64_t H,
   }
   timing_mark(5, st);
   const uint32_t ncol = cdiv(H, 64);
-  const uint32_t grid = ncol * (cdiv(N, 64) + (uint32_t)E + 1);
+  const uint32_t grid = tile_grid(ncol * (cdiv(N, 64) + (uint32_t)E + 1));
   hipLaunchKernelGGL((gemm_generic_kernel<D, false>), dim3(grid), dim3(256),
                      0, st, (const S*)act, (const S*)wd, (const S*)wd,
                      (S*)y, offsets, N, (int)I, (int)H, E, ncol, E + 1);

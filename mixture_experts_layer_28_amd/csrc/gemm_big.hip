@@ -26,11 +26,11 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kStage = (kBM + kBN) * kBK;  // elements per LDS stage
-constexpr size_t kLdsBytes = 2 * kStage * 2;
+constexpr int kBM = 256, kBK = 64;
+template <int BN> constexpr int stage_elems() { return (kBM + BN) * kBK; }
+template <int BN> constexpr size_t lds_bytes() { return 2 * stage_elems<BN>() * 2; }
 
-template <int D, bool GATEUP, int WM, int WN, bool FDB>
+template <int D, bool GATEUP, int BN, int WM, int WN, bool FDB>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
     const typename Storage<D>::T* __restrict__ A,
     const typename Storage<D>::T* __restrict__ B0,
@@ -41,18 +41,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   using S = typename Storage<D>::T;
   using V = typename Frag<D>::V;
   constexpr int NT = 64 * WM * WN;
-  constexpr int TM = kBM / WM, TN = kBN / WN;
+  constexpr int TM = kBM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int TCOLS = GATEUP ? kBN / 2 : kBN;
-  constexpr int BLK = 64 / (WM * WN);  // 1 KB LDS blocks per wave per stage
+  constexpr int TCOLS = GATEUP ? BN / 2 : BN;
+  constexpr int kStage = stage_elems<BN>();
+  constexpr int NBLK = (kBM + BN) / 8;       // 1 KB LDS blocks per stage
+  constexpr int BLK = NBLK / (WM * WN);       // ... per wave
+  static_assert(NBLK % (WM * WN) == 0, "blocks per wave");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up halves");
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   S* sm = (S*)smem_raw;
   __shared__ TileInfo ti;
 
   const int tid = threadIdx.x;
-  const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-  if (tid < 64) locate_tile(L, offsets, E, N, kBM, ncol, nseg, &ti);
+  if (tid < 64)
+    locate_tile(blockIdx.x, gridDim.x, offsets, E, N, kBM, ncol, nseg, &ti);
   __syncthreads();
   if (!ti.found) return;
   const int e = uniform(ti.e);
@@ -84,14 +87,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   const int wm = wid / WN, wn = wid % WN;
 
   // ---- global -> LDS (direct) -------------------------------------------------
-  // LDS stage: A rows 0..255 then B rows 0..255, 128 bytes per row; block b
-  // (0..63) holds rows 8b..8b+7 of that sequence.
+  // LDS stage: A rows 0..255 then B rows 0..BN-1, 128 bytes per row; block b
+  // holds rows 8b..8b+7 of that sequence.
   auto dma = [&](int k0, int st) {
     S* base = sm + st * kStage;
 #pragma unroll
     for (int j = 0; j < BLK; ++j) {
       const int b = wid + (WM * WN) * j;
-      const int r = 8 * (b & 31) + (lane >> 3);  // row within A or B
+      const int r = 8 * (b < 32 ? b : b - 32) + (lane >> 3);  // row within A or B
       const int c = (lane & 7) ^ swz(r);
       const int kk = k0 + c * 8;
       const bool kin = kk < K;
@@ -99,8 +102,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
         buffer_load_lds16(rA, base + b * 512,
                           kin ? (uint32_t)r * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
       } else {
-        const bool up = GATEUP && (b & 31) >= 16;  // uniform: rows 128..255
-        const int br = up ? r - 128 : r;
+        const bool up = GATEUP && (b - 32) * 8 >= BN / 2;  // uniform
+        const int br = up ? r - BN / 2 : r;
         buffer_load_lds16(up ? rB1 : rB0, base + b * 512,
                           kin ? (uint32_t)(n0 + br) * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
       }
@@ -114,16 +117,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // A wave whose TM rows all lie past the segment (ragged last tile) has
+  // nothing to compute; it still loads and meets the barriers.
+  const bool active = wm * TM < arows;
   auto brow = [&](int j) -> int {
     if (GATEUP) {
       constexpr int H2 = FN / 2;
       return (j < H2 ? wn * (TN / 2) + j * 16
-                     : 128 + wn * (TN / 2) + (j - H2) * 16) +
+                     : BN / 2 + wn * (TN / 2) + (j - H2) * 16) +
              (lane & 15);
     }
     return wn * TN + j * 16 + (lane & 15);
   };
   auto read_frags = [&](int st, int half, V* fa, V* fb) {
+    if (!active) return;
     const S* As = sm + st * kStage;
     const S* Bs = As + kBM * kBK;
     const int c = half * 4 + (lane >> 4);
@@ -139,6 +146,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
     }
   };
   auto mma = [&](const V* fa, const V* fb) {
+    if (!active) return;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   }
 }
 
-template <int D, bool GATEUP, int WM, int WN, bool FDB>
+template <int D, bool GATEUP, int BN, int WM, int WN, bool FDB>
 hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
                       const uint32_t* offsets, int64_t N, int K, int NB,
                       int E, int nseg, hipStream_t st) {
@@ -220,18 +228,24 @@ hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
   static bool attr = false;
   if (!attr) {
     hipError_t err = hipFuncSetAttribute(
-        (const void*)gemm_big_kernel<D, GATEUP, WM, WN, FDB>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (const void*)gemm_big_kernel<D, GATEUP, BN, WM, WN, FDB>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes<BN>());
     if (err != hipSuccess) return err;
     attr = true;
   }
-  const uint32_t ncol = cdiv(NB, GATEUP ? kBN / 2 : kBN);
-  const uint32_t grid = ncol * (cdiv(N, kBM) + (uint32_t)nseg);
-  hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP, WM, WN, FDB>), dim3(grid),
-                     dim3(64 * WM * WN), kLdsBytes, st, (const S*)A,
+  const uint32_t ncol = cdiv(NB, GATEUP ? BN / 2 : BN);
+  const uint32_t grid = tile_grid(ncol * (cdiv(N, kBM) + (uint32_t)nseg));
+  hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP, BN, WM, WN, FDB>), dim3(grid),
+                     dim3(64 * WM * WN), lds_bytes<BN>(), st, (const S*)A,
                      (const S*)B0, (const S*)B1, (S*)C, offsets, N, K, NB, E,
                      ncol, nseg);
   return hipGetLastError();
+}
+
+// Rounds of 256 concurrent workgroups a launch of `tiles` tiles takes,
+// weighted by the relative cost of one tile.
+inline double rounds(double tiles, double cost) {
+  return __builtin_ceil(tiles / 256.0) * cost;
 }
 
 template <int D, int WM, int WN, bool FDB>
@@ -239,12 +253,20 @@ hipError_t launch_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                        int E, const void* wg, const void* wu, const void* wd,
                        const uint32_t* offsets, void* act, void* y,
                        hipStream_t st) {
-  hipError_t err = launch_one<D, true, WM, WN, FDB>(xd, wg, wu, act, offsets, N,
-                                               (int)H, (int)I, E, E, st);
+  hipError_t err = launch_one<D, true, 256, WM, WN, FDB>(
+      xd, wg, wu, act, offsets, N, (int)H, (int)I, E, E, st);
   if (err != hipSuccess) return err;
   timing_mark(5, st);
-  return launch_one<D, false, WM, WN, FDB>(act, wd, wd, y, offsets, N, (int)I,
-                                      (int)H, E, E + 1, st);
+  // Down product: 256-wide column blocks unless 128-wide ones finish in
+  // fewer rounds of the CUs (a 128-wide tile costs about 0.55 of a 256-wide
+  // one).  The row-block count is estimated from N (segment sizes stay on
+  // the device).
+  const double rb = (double)cdiv(N, kBM) + 0.5 * E;
+  if (rounds(rb * cdiv(H, 128), 0.85) < rounds(rb * cdiv(H, 256), 1.0))
+    return launch_one<D, false, 128, WM, WN, FDB>(act, wd, wd, y, offsets, N,
+                                                  (int)I, (int)H, E, E + 1, st);
+  return launch_one<D, false, 256, WM, WN, FDB>(act, wd, wd, y, offsets, N,
+                                                (int)I, (int)H, E, E + 1, st);
 }
 
 template <int D>
@@ -256,6 +278,8 @@ hipError_t launch_variant(int variant, const void* xd, int64_t N, int64_t H,
     case 1: return launch_pair<D, 2, 2, true>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
     case 2: return launch_pair<D, 4, 2, false>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
     case 3: return launch_pair<D, 2, 2, false>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
+    case 4: return launch_pair<D, 4, 2, true>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
+    case 5: return launch_pair<D, 2, 4, true>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
     default: return launch_pair<D, 2, 4, false>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
   }
 }

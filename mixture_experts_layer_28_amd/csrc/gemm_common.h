@@ -13,43 +13,82 @@ struct TileInfo {
   int e, col, found;
 };
 
-// Executed by the 64 lanes of wavefront 0.  Segment s < E is
-// [offsets[s], offsets[s+1]); segment E (only if nseg > E) is
-// [offsets[E], N).  Bounds are clamped into [0, N] and made monotone so
-// that any offsets array keeps every access in bounds.
-__device__ inline void locate_tile(uint32_t L, const uint32_t* __restrict__ offsets,
-                            int E, int64_t N, int BM, uint32_t ncol, int nseg,
-                            TileInfo* ti) {
+// Segment s < E is [offsets[s], offsets[s+1]); segment E (only if
+// nseg > E) is [offsets[E], N).  Bounds are clamped into [0, N] and made
+// monotone so that any offsets array keeps every access in bounds.
+__device__ __forceinline__ void segment(const uint32_t* __restrict__ offsets,
+                                        int s, int E, int64_t N, int nseg,
+                                        int64_t* lo, int64_t* hi) {
+  *lo = *hi = 0;
+  if (s < nseg) {
+    int64_t a = offsets[s];
+    a = a < N ? a : N;
+    int64_t b = s < E ? (int64_t)offsets[s + 1] : N;
+    b = b < a ? a : (b > N ? N : b);
+    *lo = a;
+    *hi = b;
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Tile map, executed by the 64 lanes of wavefront 0 of workgroup b of G.
+//
+// The tiles are (segment, row block of BM rows, column block); only the
+// segment sizes on the device fix how many exist, so the grid is an upper
+// bound.  Pass 1 totals the real tiles; they are then split evenly over the
+// 8 XCDs (hardware deals workgroup b to XCD b % 8; each XCD takes a
+// contiguous range of logical ids, so tiles that share operands share an
+// L2), and pass 2 finds the segment of logical tile L.  Inside a segment,
+// tiles go in groups of up to 8 row blocks: all column blocks of a group
+// before the next group, the row blocks of one column block consecutive.
+// G must be a multiple of 8 and at least 8 * ceil(tiles / 8).
+__device__ inline void locate_tile(uint32_t b, uint32_t G,
+                                   const uint32_t* __restrict__ offsets,
+                                   int E, int64_t N, int BM, uint32_t ncol,
+                                   int nseg, TileInfo* ti) {
   const int lane = threadIdx.x;
   if (lane == 0) ti->found = 0;
+  uint32_t total = 0;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    int64_t lo, hi;
+    segment(offsets, s0 + lane, E, N, nseg, &lo, &hi);
+    const uint32_t cnt = (uint32_t)((hi - lo + BM - 1) / BM) * ncol;
+    total += __shfl(wave_inclusive_sum(cnt, lane), 63, 64);
+  }
+  const uint32_t per = (total + 7u) / 8u, local = b / 8u;
+  const uint32_t L = (b % 8u) * per + local;
+  if (local >= per || L >= total) return;
+  (void)G;
   uint32_t base = 0;
   for (int s0 = 0; s0 < nseg; s0 += 64) {
     const int s = s0 + lane;
-    int64_t lo = 0, hi = 0;
-    if (s < nseg) {
-      lo = offsets[s];
-      lo = lo < N ? lo : N;
-      hi = s < E ? (int64_t)offsets[s + 1] : N;
-      hi = hi < lo ? lo : (hi > N ? N : hi);
-    }
+    int64_t lo, hi;
+    segment(offsets, s, E, N, nseg, &lo, &hi);
     const uint32_t nt = (uint32_t)((hi - lo + BM - 1) / BM);
     const uint32_t cnt = nt * ncol;
-    uint32_t inc = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += t;
-    }
+    const uint32_t inc = wave_inclusive_sum(cnt, lane);
     const uint32_t exc = inc - cnt;
     const bool hit = L >= base + exc && L < base + inc;
     if (__ballot(hit)) {
       if (hit) {
-        const uint32_t local = L - base - exc;
+        const uint32_t l = L - base - exc;
+        constexpr uint32_t GM = 8;
+        const uint32_t grp = l / (GM * ncol), first = grp * GM;
+        const uint32_t gs = nt - first < GM ? nt - first : GM;
+        const uint32_t rem = l - grp * GM * ncol;
         ti->e = s;
         ti->lo = lo;
         ti->hi = hi;
-        ti->col = (int)(local / nt);
-        ti->row0 = lo + (int64_t)(local % nt) * BM;
+        ti->col = (int)(rem / gs);
+        ti->row0 = lo + (int64_t)(first + rem % gs) * BM;
         ti->found = 1;
       }
       return;
@@ -58,10 +97,10 @@ __device__ inline void locate_tile(uint32_t L, const uint32_t* __restrict__ offs
   }
 }
 
-// 16-byte chunk c of tile row r sits at chunk position c ^ swz(r) of the
-// row's 128 bytes.  Fragment reads take one chunk from 16 consecutive rows;
-// measured on gfx950, rotating by r & 7 spreads them as evenly as a
-// contiguous read.
+// Grid for an upper bound of `tiles` tiles: a multiple of 8 with at least
+// ceil(tiles / 8) workgroups on every XCD.
+inline uint32_t tile_grid(uint32_t tiles) { return 8u * ((tiles + 7u) / 8u); }
+
 __device__ __forceinline__ int swz(int r) { return r & 7; }
 
 template <int D> struct Frag;
