@@ -67,34 +67,61 @@ __global__ void dispatch_count_kernel(const uint32_t* __restrict__ idx,
   for (int b = lane; b < nb; b += 64) table[c * nb + b] = cnt[b];
 }
 
+// One workgroup of 1024 threads: P = 1024 / (bins per pass) threads share a
+// bin, each owning a contiguous run of chunks; their run sums are scanned
+// across the P threads, the bin totals across bins.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     uint32_t* __restrict__ table, int64_t nchunks, int E,
     uint32_t* __restrict__ offsets) {
-  __shared__ uint32_t sh[1024];
+  __shared__ uint32_t run_sum[1024];
+  __shared__ uint32_t bin_base[1025];
+  __shared__ uint32_t carry;
   const int tid = threadIdx.x;
   const int nb = E + 1;
-  const int per = (nb + 1023) / 1024;
-  const int b0 = tid * per < nb ? tid * per : nb;
-  const int b1 = b0 + per < nb ? b0 + per : nb;
-  uint32_t mine = 0;
-  for (int b = b0; b < b1; ++b)
-    for (int64_t c = 0; c < nchunks; ++c) mine += table[c * nb + b];
-  sh[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const uint32_t add = tid >= off ? sh[tid - off] : 0u;
+  // threads per bin: a power of two with P * min(nb, 1024) <= 1024
+  int P = 1;
+  while (P * 2 * (nb < 1024 ? nb : 1024) <= 1024) P *= 2;
+  const int bins_per_pass = 1024 / P;
+  const int lp = tid % P, bl = tid / P;
+  const int64_t per = (nchunks + P - 1) / P;
+  const int64_t c0 = lp * per < nchunks ? lp * per : nchunks;
+  const int64_t c1 = c0 + per < nchunks ? c0 + per : nchunks;
+  if (tid == 0) carry = 0;
+  for (int pass = 0; pass * bins_per_pass < nb; ++pass) {
+    const int b = pass * bins_per_pass + bl;
+    uint32_t mine = 0;
+    if (b < nb)
+      for (int64_t c = c0; c < c1; ++c) mine += table[c * nb + b];
+    run_sum[tid] = mine;
     __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
-  }
-  uint32_t run = sh[tid] - mine;  // exclusive prefix over bins
-  for (int b = b0; b < b1; ++b) {
-    offsets[b] = run;  // bins 0..E: offsets[E] is the first invalid row
-    for (int64_t c = 0; c < nchunks; ++c) {
-      const uint32_t n = table[c * nb + b];
-      table[c * nb + b] = run;
-      run += n;
+    // inclusive scan of the P run sums of each bin (Hillis-Steele)
+    for (int off = 1; off < P; off <<= 1) {
+      const uint32_t add = lp >= off ? run_sum[tid - off] : 0u;
+      __syncthreads();
+      run_sum[tid] += add;
+      __syncthreads();
     }
+    // bin totals of this pass -> exclusive prefix over all bins (serial in
+    // one thread: at most 1024 adds per pass)
+    if (tid == 0) {
+      uint32_t acc = carry;
+      for (int j = 0; j < bins_per_pass && pass * bins_per_pass + j < nb; ++j) {
+        bin_base[pass * bins_per_pass + j] = acc;
+        acc += run_sum[j * P + P - 1];
+      }
+      carry = acc;
+    }
+    __syncthreads();
+    if (b < nb) {
+      uint32_t run = bin_base[b] + run_sum[tid] - mine;
+      if (lp == 0) offsets[b] = bin_base[b];  // offsets[E] = first invalid row
+      for (int64_t c = c0; c < c1; ++c) {
+        const uint32_t n = table[c * nb + b];
+        table[c * nb + b] = run;
+        run += n;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -157,7 +184,10 @@ hipError_t launch_scatter(const void* x, void* xd, int64_t T, int64_t bytes,
 DispatchPlan plan_dispatch(int64_t T, int64_t E, int64_t k) {
   DispatchPlan p;
   p.N = T * k;
-  p.chunk = 256;
+  // one 64-entry group per chunk while that keeps at most 256 chunks, so
+  // small batches still spread over many wavefronts and the scan stays short
+  p.chunk = 64;
+  while ((p.N + p.chunk - 1) / p.chunk > 256) p.chunk *= 2;
   p.nchunks = (p.N + p.chunk - 1) / p.chunk;
   while (p.nchunks * (E + 1) > kMaxTable && p.chunk < (1 << 20)) {
     p.chunk *= 2;
