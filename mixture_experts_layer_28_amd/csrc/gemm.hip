@@ -35,8 +35,6 @@
 // A segment s = E (rows [offsets[E], N), produced by out-of-range expert
 // ids) is written as zeros by the down launch.
 
-#include <cstdlib>
-
 #include "gemm_common.h"
 
 namespace moe {
@@ -373,12 +371,8 @@ hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
   // Prefill: 256 x 256 tiles when every buffer range fits 31 bits.
   const int64_t lim = (int64_t)1 << 31;
   if (H * I * 2 < lim && 256 * H * 2 < lim && 256 * I * 2 < lim) {
-    static const int variant = [] {
-      const char* v = getenv("MOE_GEMM_VARIANT");
-      return v ? atoi(v) : 2;
-    }();
     return launch_experts_big(xd, D, N, H, I, E, wg, wu, wd, offsets, act, y,
-                              variant, st);
+                              st);
   }
   return launch_mfma_pair<D, 128, 128, 2>(xd, N, H, I, E, wg, wu, wd,
                                           offsets, act, y, st);

@@ -4,22 +4,25 @@
 // src/moe/experts.rs", forward_dispatched_with_strategy: gate/up products
 // with SiLU(gate)*up, then the down product), sized for MI355X:
 //
-// * 256 x 256 output tile per workgroup of WM x WN wavefronts; a wave owns
-//   a (256/WM) x (256/WN) block of v_mfma_f32_16x16x32 tiles with FP32
-//   accumulators.  The gate+up tile holds rows [n0, n0+128) of W_gate in
-//   B rows 0..127 and the same rows of W_up in 128..255; each wave takes
-//   matching halves, so one lane holds g and u of the same output.
+// * 256 x 256 output tile per workgroup of 8 wavefronts in a 4 x 2 grid;
+//   a wave owns 64 x 128 outputs as 4 x 8 v_mfma_f32_16x16x32 tiles with
+//   FP32 accumulators, two waves per SIMD (one hides the other's LDS
+//   latency).  The gate+up tile holds rows [n0, n0+128) of W_gate in B rows
+//   0..127 and the same rows of W_up in 128..255; each wave takes matching
+//   halves, so one lane holds g and u of the same output.
 // * Operand tiles reach LDS without passing through registers: the buffer
 //   unit writes LDS directly (buffer_load_dwordx4 ... lds, 16 bytes per
 //   lane), one 1 KB block of 8 tile rows per instruction; each lane fetches
 //   the global chunk that the row swizzle maps to its LDS slot.  Reads past
 //   a segment's last row, a weight matrix's last row or K come back as
-//   zeros (raw buffer range checks), so ragged tiles need no clamping.
-// * Two LDS stages of K = 64 (128 KB).  Per stage a wave runs two K = 32
-//   halves; the fragments of the next half are read from LDS while the
-//   current half's MFMAs run, and the single barrier per stage sits between
-//   the halves.  The loads of stage k+2 are issued right after that
-//   barrier, so they have a full stage to land.
+//   zeros (raw buffer range checks), so ragged tiles need no clamping; A
+//   blocks wholly past the segment are not loaded and waves whose rows all
+//   lie past it skip their MFMAs.
+// * Two LDS stages of K = 64 (128 KB, one workgroup per CU) and one barrier
+//   per stage; the loads of stage k+2 go out right after the barrier that
+//   ends stage k, so they have a whole stage of MFMAs to land.
+// * Measured on MI355X: this kernel is bound by operand delivery into the
+//   CUs (global -> LDS), not by the MFMA or LDS-read rates.
 
 #include "gemm_common.h"
 
@@ -30,7 +33,7 @@ constexpr int kBM = 256, kBK = 64;
 template <int BN> constexpr int stage_elems() { return (kBM + BN) * kBK; }
 template <int BN> constexpr size_t lds_bytes() { return 2 * stage_elems<BN>() * 2; }
 
-template <int D, bool GATEUP, int BN, int WM, int WN, bool FDB>
+template <int D, bool GATEUP, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
     const typename Storage<D>::T* __restrict__ A,
     const typename Storage<D>::T* __restrict__ B0,
@@ -99,8 +102,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
       const int kk = k0 + c * 8;
       const bool kin = kk < K;
       if (b < 32) {
-        buffer_load_lds16(rA, base + b * 512,
-                          kin ? (uint32_t)r * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
+        // blocks wholly past the segment stay unloaded: only rows below
+        // arows are ever stored, and the skip keeps a ragged tile's memory
+        // traffic to its real rows (the uniform test costs no divergence)
+        if (8 * b < arows)
+          buffer_load_lds16(rA, base + b * 512,
+                            kin ? (uint32_t)r * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
       } else {
         const bool up = GATEUP && (b - 32) * 8 >= BN / 2;  // uniform
         const int br = up ? r - BN / 2 : r;
@@ -157,36 +164,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   dma(0, 0);
   wait_vmem();
   __syncthreads();
-  if (FDB) {
-    // fragments of the next K = 32 half are read during the current half
-    V fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-    read_frags(0, 0, fa0, fb0);
-    if (nk > 1) dma(kBK, 1);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      read_frags(st, 1, fa1, fb1);
-      mma(fa0, fb0);
+  if (nk > 1) dma(kBK, 1);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    V fa[FM], fb[FN];
+    read_frags(st, 0, fa, fb);
+    mma(fa, fb);
+    read_frags(st, 1, fa, fb);
+    mma(fa, fb);
+    if (kt + 1 < nk) {
       wait_vmem();
       __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
-      if (kt + 1 < nk) read_frags(st ^ 1, 0, fa0, fb0);
       if (kt + 2 < nk) dma((kt + 2) * kBK, st);
-      mma(fa1, fb1);
-    }
-  } else {
-    // the other wave on the SIMD covers the fragment-read latency
-    if (nk > 1) dma(kBK, 1);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      V fa[FM], fb[FN];
-      read_frags(st, 0, fa, fb);
-      mma(fa, fb);
-      read_frags(st, 1, fa, fb);
-      mma(fa, fb);
-      if (kt + 1 < nk) {
-        wait_vmem();
-        __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
-        if (kt + 2 < nk) dma((kt + 2) * kBK, st);
-      }
     }
   }
 
@@ -220,7 +209,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   }
 }
 
-template <int D, bool GATEUP, int BN, int WM, int WN, bool FDB>
+template <int D, bool GATEUP, int BN, int WM, int WN>
 hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
                       const uint32_t* offsets, int64_t N, int K, int NB,
                       int E, int nseg, hipStream_t st) {
@@ -228,60 +217,31 @@ hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
   static bool attr = false;
   if (!attr) {
     hipError_t err = hipFuncSetAttribute(
-        (const void*)gemm_big_kernel<D, GATEUP, BN, WM, WN, FDB>,
+        (const void*)gemm_big_kernel<D, GATEUP, BN, WM, WN>,
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes<BN>());
     if (err != hipSuccess) return err;
     attr = true;
   }
   const uint32_t ncol = cdiv(NB, GATEUP ? BN / 2 : BN);
   const uint32_t grid = tile_grid(ncol * (cdiv(N, kBM) + (uint32_t)nseg));
-  hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP, BN, WM, WN, FDB>), dim3(grid),
+  hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP, BN, WM, WN>), dim3(grid),
                      dim3(64 * WM * WN), lds_bytes<BN>(), st, (const S*)A,
                      (const S*)B0, (const S*)B1, (S*)C, offsets, N, K, NB, E,
                      ncol, nseg);
   return hipGetLastError();
 }
 
-// Rounds of 256 concurrent workgroups a launch of `tiles` tiles takes,
-// weighted by the relative cost of one tile.
-inline double rounds(double tiles, double cost) {
-  return __builtin_ceil(tiles / 256.0) * cost;
-}
-
-template <int D, int WM, int WN, bool FDB>
+template <int D>
 hipError_t launch_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                        int E, const void* wg, const void* wu, const void* wd,
                        const uint32_t* offsets, void* act, void* y,
                        hipStream_t st) {
-  hipError_t err = launch_one<D, true, 256, WM, WN, FDB>(
+  hipError_t err = launch_one<D, true, 256, 4, 2>(
       xd, wg, wu, act, offsets, N, (int)H, (int)I, E, E, st);
   if (err != hipSuccess) return err;
   timing_mark(5, st);
-  // Down product: 256-wide column blocks unless 128-wide ones finish in
-  // fewer rounds of the CUs (a 128-wide tile costs about 0.55 of a 256-wide
-  // one).  The row-block count is estimated from N (segment sizes stay on
-  // the device).
-  const double rb = (double)cdiv(N, kBM) + 0.5 * E;
-  if (rounds(rb * cdiv(H, 128), 0.85) < rounds(rb * cdiv(H, 256), 1.0))
-    return launch_one<D, false, 128, WM, WN, FDB>(act, wd, wd, y, offsets, N,
-                                                  (int)I, (int)H, E, E + 1, st);
-  return launch_one<D, false, 256, WM, WN, FDB>(act, wd, wd, y, offsets, N,
-                                                (int)I, (int)H, E, E + 1, st);
-}
-
-template <int D>
-hipError_t launch_variant(int variant, const void* xd, int64_t N, int64_t H,
-                          int64_t I, int E, const void* wg, const void* wu,
-                          const void* wd, const uint32_t* offsets, void* act,
-                          void* y, hipStream_t st) {
-  switch (variant) {
-    case 1: return launch_pair<D, 2, 2, true>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
-    case 2: return launch_pair<D, 4, 2, false>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
-    case 3: return launch_pair<D, 2, 2, false>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
-    case 4: return launch_pair<D, 4, 2, true>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
-    case 5: return launch_pair<D, 2, 4, true>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
-    default: return launch_pair<D, 2, 4, false>(xd, N, H, I, E, wg, wu, wd, offsets, act, y, st);
-  }
+  return launch_one<D, false, 256, 4, 2>(act, wd, wd, y, offsets, N, (int)I,
+                                         (int)H, E, E + 1, st);
 }
 
 }  // namespace
@@ -290,12 +250,12 @@ hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
                               int64_t I, int E, const void* w_gate,
                               const void* w_up, const void* w_down,
                               const uint32_t* offsets, void* act, void* y,
-                              int variant, hipStream_t st) {
+                              hipStream_t st) {
   if (dt == DT_BF16)
-    return launch_variant<DT_BF16>(variant, xd, N, H, I, E, w_gate, w_up,
-                                   w_down, offsets, act, y, st);
-  return launch_variant<DT_F16>(variant, xd, N, H, I, E, w_gate, w_up, w_down,
-                                offsets, act, y, st);
+    return launch_pair<DT_BF16>(xd, N, H, I, E, w_gate, w_up, w_down, offsets,
+                                act, y, st);
+  return launch_pair<DT_F16>(xd, N, H, I, E, w_gate, w_up, w_down, offsets,
+                             act, y, st);
 }
 
 }  // namespace moe

@@ -50,7 +50,7 @@ hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
                               int64_t I, int E, const void* w_gate,
                               const void* w_up, const void* w_down,
                               const uint32_t* offsets, void* act, void* y,
-                              int variant, hipStream_t st);
+                              hipStream_t st);
 
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(const void* y, int dt, int64_t N, int64_t T,
