@@ -4,37 +4,45 @@
 // src/moe/experts.rs", forward_dispatched_with_strategy: gate/up products
 // with SiLU(gate)*up, then the down product), sized for MI355X:
 //
-// * 256 x 256 output tile per workgroup of 8 wavefronts in a 4 x 2 grid;
-//   a wave owns 64 x 128 outputs as 4 x 8 v_mfma_f32_16x16x32 tiles with
-//   FP32 accumulators, two waves per SIMD (one hides the other's LDS
-//   latency).  The gate+up tile holds rows [n0, n0+128) of W_gate in B rows
-//   0..127 and the same rows of W_up in 128..255; each wave takes matching
-//   halves, so one lane holds g and u of the same output.
+// * Row blocks of up to 320 rows x 256 columns per workgroup of 8
+//   wavefronts in a 4 x 2 grid.  A segment of R rows is cut into
+//   ceil(R / 320) row blocks of equal size (+-1 row), so a segment a few rows
+//   longer than a multiple of 256 does not leave a thin last block that
+//   costs a whole pass over the weights; Mixtral-sized segments of about
+//   1000-1070 rows become 4 blocks of 246-267 rows.  The 16-row MFMA row
+//   tiles of a block are shared out over the 4 wave rows as evenly as
+//   possible (at most 5 each); a wave owns up to 80 x 128 outputs as
+//   v_mfma_f32_16x16x32 tiles with FP32 accumulators, two waves per SIMD.
+//   The gate+up tile holds rows [n0, n0+128) of W_gate in B rows 0..127 and
+//   the same rows of W_up in 128..255; each wave takes matching halves, so
+//   one lane holds g and u of the same output.
 // * Operand tiles reach LDS without passing through registers: the buffer
 //   unit writes LDS directly (buffer_load_dwordx4 ... lds, 16 bytes per
 //   lane), one 1 KB block of 8 tile rows per instruction; each lane fetches
 //   the global chunk that the row swizzle maps to its LDS slot.  Reads past
-//   a segment's last row, a weight matrix's last row or K come back as
-//   zeros (raw buffer range checks), so ragged tiles need no clamping; A
-//   blocks wholly past the segment are not loaded and waves whose rows all
-//   lie past it skip their MFMAs.
-// * Two LDS stages of K = 64 (128 KB, one workgroup per CU) and one barrier
-//   per stage; the loads of stage k+2 go out right after the barrier that
-//   ends stage k, so they have a whole stage of MFMAs to land.
+//   a block's last row, a weight matrix's last row or K come back as zeros
+//   (raw buffer range checks), so ragged tiles need no clamping; A blocks
+//   wholly past the row block are not loaded.
+// * Two LDS stages of K = 64 (2 x 72 KB, one workgroup per CU) and one
+//   barrier per stage; the loads of stage k+2 go out right after the
+//   barrier that ends stage k, so they have a whole stage of MFMAs to land.
 // * Measured on MI355X: this kernel is bound by operand delivery into the
 //   CUs (global -> LDS), not by the MFMA or LDS-read rates.
 
 #include "gemm_common.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
-constexpr int kBM = 256, kBK = 64;
-template <int BN> constexpr int stage_elems() { return (kBM + BN) * kBK; }
-template <int BN> constexpr size_t lds_bytes() { return 2 * stage_elems<BN>() * 2; }
+constexpr int kBM = 320, kBN = 256, kBK = 64;
+constexpr int kFM = kBM / 4 / 16;                 // MFMA row tiles per wave, at most
+constexpr int kStage = (kBM + kBN) * kBK;         // elements of one LDS stage
+constexpr size_t kLds = 2 * kStage * 2;           // two stages of 16-bit data
 
-template <int D, bool GATEUP, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
+template <int D, bool GATEUP>
+__global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const typename Storage<D>::T* __restrict__ A,
     const typename Storage<D>::T* __restrict__ B0,
     const typename Storage<D>::T* __restrict__ B1,
@@ -43,14 +51,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
     uint32_t ncol, int nseg) {
   using S = typename Storage<D>::T;
   using V = typename Frag<D>::V;
-  constexpr int NT = 64 * WM * WN;
-  constexpr int TM = kBM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int TCOLS = GATEUP ? BN / 2 : BN;
-  constexpr int kStage = stage_elems<BN>();
-  constexpr int NBLK = (kBM + BN) / 8;       // 1 KB LDS blocks per stage
-  constexpr int BLK = NBLK / (WM * WN);       // ... per wave
-  static_assert(NBLK % (WM * WN) == 0, "blocks per wave");
+  constexpr int WN = 2, NT = 512;
+  constexpr int TN = kBN / WN;                    // 128 columns per wave
+  constexpr int FN = TN / 16;                     // 8 MFMA column tiles
+  constexpr int TCOLS = GATEUP ? kBN / 2 : kBN;
+  constexpr int NBLK = (kBM + kBN) / 8;           // 1 KB LDS blocks per stage
+  constexpr int ABLK = kBM / 8;
+  constexpr int BLK = NBLK / 8;                   // ... per wave
+  static_assert(NBLK % 8 == 0, "blocks per wave");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up halves");
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   S* sm = (S*)smem_raw;
@@ -58,17 +66,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
 
   const int tid = threadIdx.x;
   if (tid < 64)
-    locate_tile(blockIdx.x, gridDim.x, offsets, E, N, kBM, ncol, nseg, &ti);
+    locate_tile(blockIdx.x, gridDim.x, offsets, E, N, kBM, ncol, nseg, &ti,
+                true);
   __syncthreads();
   if (!ti.found) return;
   const int e = uniform(ti.e);
-  const int64_t hi = uniform(ti.hi), row0 = uniform(ti.row0);
+  const int64_t row0 = uniform(ti.row0);
+  const int arows = uniform(ti.rows);             // 1 .. kBM
+  const int64_t tend = row0 + arows;
   const int64_t n0 = (int64_t)uniform(ti.col) * TCOLS;
 
   if (e >= E) {  // rows of out-of-range experts: zeros
     for (int q = tid; q < kBM * TCOLS; q += NT) {
       const int64_t r = row0 + q / TCOLS, c = n0 + q % TCOLS;
-      if (r < hi && c < NB) C[r * NB + c] = from_f32<D>(0.0f);
+      if (r < tend && c < NB) C[r * NB + c] = from_f32<D>(0.0f);
     }
     return;
   }
@@ -76,7 +87,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   const uint32_t rowbytes = (uint32_t)K * sizeof(S);
   // the A resource spans this tile's rows only, so every range fits in
   // 31 bits and OOB (2^31) is always past the end
-  const int64_t arows = hi - row0 < kBM ? hi - row0 : kBM;
   const __amdgpu_buffer_rsrc_t rA =
       make_rsrc(A + row0 * K, (uint64_t)arows * rowbytes);
   const uint64_t wbytes = (uint64_t)NB * rowbytes;
@@ -89,28 +99,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   const int wid = uniform(tid >> 6), lane = tid & 63;
   const int wm = wid / WN, wn = wid % WN;
 
+  // MFMA row tiles of this wave: t16 tiles over 4 wave rows, the first
+  // t16 % 4 rows taking one more; waves wm and wm + 2 share a SIMD.
+  const int t16 = (arows + 15) >> 4;
+  const int fm = (t16 >> 2) + (wm < (t16 & 3) ? 1 : 0);
+  const int tr0 = 16 * (wm * (t16 >> 2) + (wm < (t16 & 3) ? wm : (t16 & 3)));
+
   // ---- global -> LDS (direct) -------------------------------------------------
-  // LDS stage: A rows 0..255 then B rows 0..BN-1, 128 bytes per row; block b
-  // holds rows 8b..8b+7 of that sequence.
+  // LDS stage: A rows 0..kBM-1 then B rows 0..255, 128 bytes per row; block
+  // b holds rows 8b..8b+7 of that sequence.
   auto dma = [&](int k0, int st) {
     S* base = sm + st * kStage;
 #pragma unroll
     for (int j = 0; j < BLK; ++j) {
-      const int b = wid + (WM * WN) * j;
-      const int r = 8 * (b < 32 ? b : b - 32) + (lane >> 3);  // row within A or B
+      const int b = wid + 8 * j;
+      const int r = 8 * (b < ABLK ? b : b - ABLK) + (lane >> 3);  // row within A or B
       const int c = (lane & 7) ^ swz(r);
       const int kk = k0 + c * 8;
       const bool kin = kk < K;
-      if (b < 32) {
-        // blocks wholly past the segment stay unloaded: only rows below
-        // arows are ever stored, and the skip keeps a ragged tile's memory
-        // traffic to its real rows (the uniform test costs no divergence)
+      if (b < ABLK) {
+        // blocks wholly past the row block stay unloaded (a uniform test)
         if (8 * b < arows)
           buffer_load_lds16(rA, base + b * 512,
                             kin ? (uint32_t)r * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
       } else {
-        const bool up = GATEUP && (b - 32) * 8 >= BN / 2;  // uniform
-        const int br = up ? r - BN / 2 : r;
+        const bool up = GATEUP && (b - ABLK) * 8 >= kBN / 2;  // uniform
+        const int br = up ? r - kBN / 2 : r;
         buffer_load_lds16(up ? rB1 : rB0, base + b * 512,
                           kin ? (uint32_t)(n0 + br) * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
       }
@@ -118,74 +132,85 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   };
 
   // ---- fragments and MFMAs ----------------------------------------------------
-  f32x4 acc[FM][FN];
+  f32x4 acc[kFM][FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // A wave whose TM rows all lie past the segment (ragged last tile) has
-  // nothing to compute; it still loads and meets the barriers.
-  const bool active = wm * TM < arows;
   auto brow = [&](int j) -> int {
     if (GATEUP) {
       constexpr int H2 = FN / 2;
       return (j < H2 ? wn * (TN / 2) + j * 16
-                     : BN / 2 + wn * (TN / 2) + (j - H2) * 16) +
+                     : kBN / 2 + wn * (TN / 2) + (j - H2) * 16) +
              (lane & 15);
     }
     return wn * TN + j * 16 + (lane & 15);
   };
-  auto read_frags = [&](int st, int half, V* fa, V* fb) {
-    if (!active) return;
-    const S* As = sm + st * kStage;
-    const S* Bs = As + kBM * kBK;
-    const int c = half * 4 + (lane >> 4);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = wm * TM + i * 16 + (lane & 15);
-      fa[i] = *(const V*)&As[r * kBK + ((c ^ swz(r)) << 3)];
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = brow(j);
-      fb[j] = *(const V*)&Bs[r * kBK + ((c ^ swz(r)) << 3)];
-    }
-  };
-  auto mma = [&](const V* fa, const V* fb) {
-    if (!active) return;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
-  };
 
   const int nk = (K + kBK - 1) / kBK;
-  dma(0, 0);
-  wait_vmem();
-  __syncthreads();
-  if (nk > 1) dma(kBK, 1);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    V fa[FM], fb[FN];
-    read_frags(st, 0, fa, fb);
-    mma(fa, fb);
-    read_frags(st, 1, fa, fb);
-    mma(fa, fb);
-    if (kt + 1 < nk) {
-      wait_vmem();
-      __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
-      if (kt + 2 < nk) dma((kt + 2) * kBK, st);
+  // The K loop for a wave with FMC MFMA row tiles (0: it only loads).
+  auto kloop = [&](auto fm_c) {
+    constexpr int FMC = decltype(fm_c)::value;
+    auto read_frags = [&](int st, int half, V* fa, V* fb) {
+      const S* As = sm + st * kStage;
+      const S* Bs = As + kBM * kBK;
+      const int c = half * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < FMC; ++i) {
+        const int r = tr0 + i * 16 + (lane & 15);
+        fa[i] = *(const V*)&As[r * kBK + ((c ^ swz(r)) << 3)];
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = brow(j);
+        fb[j] = *(const V*)&Bs[r * kBK + ((c ^ swz(r)) << 3)];
+      }
+    };
+    auto mma = [&](const V* fa, const V* fb) {
+#pragma unroll
+      for (int i = 0; i < FMC; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
+    };
+    dma(0, 0);
+    wait_vmem();
+    __syncthreads();
+    if (nk > 1) dma(kBK, 1);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      if constexpr (FMC > 0) {
+        V fa[FMC], fb[FN];
+        read_frags(st, 0, fa, fb);
+        mma(fa, fb);
+        read_frags(st, 1, fa, fb);
+        mma(fa, fb);
+      }
+      if (kt + 1 < nk) {
+        wait_vmem();
+        __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
+        if (kt + 2 < nk) dma((kt + 2) * kBK, st);
+      }
     }
+  };
+  switch (fm) {
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
   }
 
   // ---- epilogue ---------------------------------------------------------------
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < kFM; ++i) {
+    if (i >= fm) break;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t r = row0 + wm * TM + i * 16 + (lane >> 4) * 4 + q;
-      if (r >= hi) continue;
+      const int64_t r = row0 + tr0 + i * 16 + (lane >> 4) * 4 + q;
+      if (r >= tend) continue;
       S* crow = C + r * NB;
       if (GATEUP) {
         constexpr int H2 = FN / 2;
@@ -209,7 +234,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(
   }
 }
 
-template <int D, bool GATEUP, int BN, int WM, int WN>
+template <int D, bool GATEUP>
 hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
                       const uint32_t* offsets, int64_t N, int K, int NB,
                       int E, int nseg, hipStream_t st) {
@@ -217,17 +242,17 @@ hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
   static bool attr = false;
   if (!attr) {
     hipError_t err = hipFuncSetAttribute(
-        (const void*)gemm_big_kernel<D, GATEUP, BN, WM, WN>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes<BN>());
+        (const void*)gemm_big_kernel<D, GATEUP>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (err != hipSuccess) return err;
     attr = true;
   }
-  const uint32_t ncol = cdiv(NB, GATEUP ? BN / 2 : BN);
+  const uint32_t ncol = cdiv(NB, GATEUP ? kBN / 2 : kBN);
+  // sum over segments of ceil(rows / kBM) <= ceil(N / kBM) + nseg
   const uint32_t grid = tile_grid(ncol * (cdiv(N, kBM) + (uint32_t)nseg));
-  hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP, BN, WM, WN>), dim3(grid),
-                     dim3(64 * WM * WN), lds_bytes<BN>(), st, (const S*)A,
-                     (const S*)B0, (const S*)B1, (S*)C, offsets, N, K, NB, E,
-                     ncol, nseg);
+  hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP>), dim3(grid), dim3(512),
+                     kLds, st, (const S*)A, (const S*)B0, (const S*)B1, (S*)C,
+                     offsets, N, K, NB, E, ncol, nseg);
   return hipGetLastError();
 }
 
@@ -236,12 +261,12 @@ hipError_t launch_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                        int E, const void* wg, const void* wu, const void* wd,
                        const uint32_t* offsets, void* act, void* y,
                        hipStream_t st) {
-  hipError_t err = launch_one<D, true, 256, 4, 2>(
-      xd, wg, wu, act, offsets, N, (int)H, (int)I, E, E, st);
+  hipError_t err = launch_one<D, true>(xd, wg, wu, act, offsets, N, (int)H,
+                                       (int)I, E, E, st);
   if (err != hipSuccess) return err;
   timing_mark(5, st);
-  return launch_one<D, false, 256, 4, 2>(act, wd, wd, y, offsets, N, (int)I,
-                                         (int)H, E, E + 1, st);
+  return launch_one<D, false>(act, wd, wd, y, offsets, N, (int)I, (int)H, E,
+                              E + 1, st);
 }
 
 }  // namespace

@@ -9,8 +9,9 @@
 namespace moe {
 
 struct TileInfo {
-  int64_t lo, hi, row0;
+  int64_t lo, hi, row0;  // segment [lo, hi); the tile's first row
   int e, col, found;
+  int rows;              // rows of the tile: [row0, row0 + rows)
 };
 
 // Segment s < E is [offsets[s], offsets[s+1]); segment E (only if
@@ -41,19 +42,23 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 
 // Tile map, executed by the 64 lanes of wavefront 0 of workgroup b of G.
 //
-// The tiles are (segment, row block of BM rows, column block); only the
-// segment sizes on the device fix how many exist, so the grid is an upper
-// bound.  Pass 1 totals the real tiles; they are then split evenly over the
-// 8 XCDs (hardware deals workgroup b to XCD b % 8; each XCD takes a
-// contiguous range of logical ids, so tiles that share operands share an
-// L2), and pass 2 finds the segment of logical tile L.  Inside a segment,
-// tiles go in groups of up to 8 row blocks: all column blocks of a group
-// before the next group, the row blocks of one column block consecutive.
+// The tiles are (segment, row block, column block); only the segment sizes
+// on the device fix how many exist, so the grid is an upper bound.  A
+// segment of R rows has ceil(R / BM) row blocks: of BM rows each (the last
+// one shorter) or, with `balanced`, of floor or ceil of R / ceil(R / BM)
+// rows each, so that no row block is a thin remainder.  Pass 1 totals the
+// real tiles; they are then split evenly over the 8 XCDs (hardware deals
+// workgroup b to XCD b % 8; each XCD takes a contiguous range of logical
+// ids, so tiles that share operands share an L2), and pass 2 finds the
+// segment of logical tile L.  Inside a segment, tiles go in groups of up to
+// 8 row blocks: all column blocks of a group before the next group, the row
+// blocks of one column block consecutive.
 // G must be a multiple of 8 and at least 8 * ceil(tiles / 8).
 __device__ inline void locate_tile(uint32_t b, uint32_t G,
                                    const uint32_t* __restrict__ offsets,
                                    int E, int64_t N, int BM, uint32_t ncol,
-                                   int nseg, TileInfo* ti) {
+                                   int nseg, TileInfo* ti,
+                                   bool balanced = false) {
   const int lane = threadIdx.x;
   if (lane == 0) ti->found = 0;
   uint32_t total = 0;
@@ -88,7 +93,15 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
         ti->lo = lo;
         ti->hi = hi;
         ti->col = (int)(rem / gs);
-        ti->row0 = lo + (int64_t)(first + rem % gs) * BM;
+        const int64_t rb = first + rem % gs, R = hi - lo;
+        if (balanced) {
+          const int64_t a = rb * R / nt, z = (rb + 1) * R / nt;
+          ti->row0 = lo + a;
+          ti->rows = (int)(z - a);
+        } else {
+          ti->row0 = lo + rb * BM;
+          ti->rows = (int)(hi - ti->row0 < BM ? hi - ti->row0 : BM);
+        }
         ti->found = 1;
       }
       return;
