@@ -22,7 +22,46 @@ template <> struct Vec<DT_F32> { static constexpr int n = 4; };
 template <> struct Vec<DT_F16> { static constexpr int n = 8; };
 template <> struct Vec<DT_BF16> { static constexpr int n = 8; };
 
-template <int D, int WD, int NV>
+// One output vector: slots in order; a row id >= N makes it NaN.  With KC
+// (the top-k) known at compile time every slot's load is issued before
+// the first multiply-add, so a thread has KC loads in flight.
+template <int D, int NV, int KC>
+__device__ __forceinline__ void combine_vec(
+    const typename Storage<D>::T* __restrict__ y, int64_t N, int64_t H,
+    int k, const uint32_t* rows, const float* wts, int64_t v, float* acc) {
+  using S = typename Storage<D>::T;
+  constexpr int KN = KC > 0 ? KC : 1;
+  const int kk = KC > 0 ? KC : k;
+  for (int j0 = 0; j0 < kk; j0 += KN) {
+    S vals[KN][NV];
+#pragma unroll
+    for (int j = 0; j < KN; ++j) {
+      const uint32_t r = rows[j0 + j];
+      if (r < (uint64_t)N) {
+        if constexpr (NV * sizeof(S) == 16) {
+          *(u32x4*)vals[j] = *(const u32x4*)(y + (int64_t)r * H + v * NV);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NV; ++i) vals[j][i] = y[(int64_t)r * H + v * NV + i];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KN; ++j) {
+      const uint32_t r = rows[j0 + j];
+      const float wt = wts[j0 + j];
+      if (r < (uint64_t)N) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] = fmaf(wt, to_f32<D>(vals[j][i]), acc[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] = __builtin_nanf("");
+      }
+    }
+  }
+}
+
+template <int D, int WD, int NV, int KC>
 __global__ __launch_bounds__(256) void combine_kernel(
     const typename Storage<D>::T* __restrict__ y, int64_t N, int64_t T,
     int64_t H, int k, const typename Storage<WD>::T* __restrict__ w,
@@ -51,29 +90,13 @@ __global__ __launch_bounds__(256) void combine_kernel(
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const uint32_t r = srow[tl * k + j];
-      const float wt = sw[tl * k + j];
-      if (r < (uint64_t)N) {
-        S vals[NV];
-        if constexpr (NV * sizeof(S) == 16) {
-          *(uint4*)vals = *(const uint4*)(y + (int64_t)r * H + v * NV);
-        } else {
-#pragma unroll
-          for (int i = 0; i < NV; ++i) vals[i] = y[(int64_t)r * H + v * NV + i];
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) acc[i] = fmaf(wt, to_f32<D>(vals[i]), acc[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) acc[i] = __builtin_nanf("");
-      }
-    }
+    combine_vec<D, NV, KC>(y, N, H, k, srow + tl * k, sw + tl * k, v, acc);
     S res[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) res[i] = from_f32<D>(acc[i]);
+    // the output is written once and not read back here: stream it
     if constexpr (NV * sizeof(S) == 16) {
-      *(uint4*)(out + t * H + v * NV) = *(const uint4*)res;
+      __builtin_nontemporal_store(*(const u32x4*)res, (u32x4*)(out + t * H + v * NV));
     } else {
 #pragma unroll
       for (int i = 0; i < NV; ++i) out[t * H + v * NV + i] = res[i];
@@ -81,12 +104,32 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
+template <int D, int WD, int NV>
+void launch_ck(const void* y, int64_t N, int64_t T, int64_t H, int k,
+               const void* w, const uint32_t* token_row, void* out,
+               dim3 grid, size_t lds, int tpb, hipStream_t st) {
+  using S = typename Storage<D>::T;
+  using SW = typename Storage<WD>::T;
+#define MOE_COMBINE(KC)                                                        \
+  hipLaunchKernelGGL((combine_kernel<D, WD, NV, KC>), grid, dim3(256), lds, st, \
+                     (const S*)y, N, T, H, k, (const SW*)w, token_row, (S*)out, \
+                     tpb)
+  switch (k) {
+    case 1: MOE_COMBINE(1); break;
+    case 2: MOE_COMBINE(2); break;
+    case 4: MOE_COMBINE(4); break;
+    case 6: MOE_COMBINE(6); break;
+    case 8: MOE_COMBINE(8); break;
+    default: MOE_COMBINE(0); break;
+  }
+#undef MOE_COMBINE
+}
+
 template <int D, int WD>
 hipError_t launch_c(const void* y, int64_t N, int64_t T, int64_t H, int k,
                     const void* w, const uint32_t* token_row, void* out,
                     hipStream_t st) {
   using S = typename Storage<D>::T;
-  using SW = typename Storage<WD>::T;
   constexpr int NV = Vec<D>::n;
   const bool vec_ok = H % NV == 0 && ((uintptr_t)y % 16 == 0) &&
                       ((uintptr_t)out % 16 == 0);
@@ -97,15 +140,11 @@ hipError_t launch_c(const void* y, int64_t N, int64_t T, int64_t H, int k,
   if (tpb < 1) tpb = 1;
   const dim3 grid((unsigned)((T + tpb - 1) / tpb));
   const size_t lds = (size_t)tpb * k * 8;
-  if (vec_ok) {
-    hipLaunchKernelGGL((combine_kernel<D, WD, NV>), grid, dim3(256), lds, st,
-                       (const S*)y, N, T, H, k, (const SW*)w, token_row,
-                       (S*)out, (int)tpb);
-  } else {
-    hipLaunchKernelGGL((combine_kernel<D, WD, 1>), grid, dim3(256), lds, st,
-                       (const S*)y, N, T, H, k, (const SW*)w, token_row,
-                       (S*)out, (int)tpb);
-  }
+  if (vec_ok)
+    launch_ck<D, WD, NV>(y, N, T, H, k, w, token_row, out, grid, lds, (int)tpb, st);
+  else
+    launch_ck<D, WD, 1>(y, N, T, H, k, w, token_row, out, grid, lds, (int)tpb, st);
+  (void)sizeof(S);
   return hipGetLastError();
 }
 
