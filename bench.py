@@ -51,6 +51,15 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run one plain device copy of COPY_BYTES (for "
                         "scaling the FETCH_SIZE/WRITE_SIZE counters)")
+    p.add_argument("--record-traffic", nargs=2, metavar=("PROF_DIR", "COPY_DIR"),
+                   help="no GPU work: read the rocprofv3 FETCH_SIZE and "
+                        "WRITE_SIZE runs under PROF_DIR/{fetch,write} (this "
+                        "workload) and COPY_DIR/{fetch,write} (the copy "
+                        "calibration), update profiles/traffic.json and print "
+                        "a markdown table")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="no GPU work: print the kernel statistics of a "
+                        "rocprofv3 --kernel-trace --stats run as markdown")
     return p.parse_args()
 
 
@@ -96,23 +105,133 @@ def algorithmic(wl, counts):
     }
 
 
+TRAFFIC_SOURCES = [
+    "mixture_experts_layer_28_amd/csrc/gemm_big.hip",
+    "mixture_experts_layer_28_amd/csrc/gemm_common.h",
+    "mixture_experts_layer_28_amd/csrc/device_common.h",
+    "mixture_experts_layer_28_amd/csrc/gemm.hip",
+]
+# kernel-name fragment of each timed kernel whose traffic is recorded
+TRAFFIC_KERNELS = {"gateup_gemm": "gemm_big_kernel<2, true",
+                   "down_gemm": "gemm_big_kernel<2, false"}
+
+
+def _counter_rows(run_dir):
+    """{dispatch id: (kernel name, summed counter value)} of one rocprofv3
+    --pmc run with a single counter (values summed over its instances)."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                d = int(r["Dispatch_Id"])
+                name, v = out.get(d, (r["Kernel_Name"], 0.0))
+                out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def _sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for src in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def record_traffic(workload, prof_dir, copy_dir):
+    """Scale the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the
+    timed kernels by what the same counters read for the plain copy of
+    COPY_BYTES, and store the per-launch HBM bytes in profiles/traffic.json."""
+    def last_value(run):
+        rows = _counter_rows(run)
+        return rows[max(rows)][1]
+    cf, cw = last_value(os.path.join(copy_dir, "fetch")), last_value(
+        os.path.join(copy_dir, "write"))
+    fetch_factor = COPY_BYTES / 1024.0 / cf
+    write_factor = COPY_BYTES / 1024.0 / cw
+    fetch = _counter_rows(os.path.join(prof_dir, "fetch"))
+    write = _counter_rows(os.path.join(prof_dir, "write"))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        doc = {}
+    doc["about"] = (
+        "HBM traffic per launch of the dominant kernels, from two rocprofv3 "
+        "--pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) of "
+        "bench.py, each scaled by what the same counter reads for a plain "
+        "4 GiB device copy (bench.py --copy-calibration).  Written by "
+        "bench.py --record-traffic; bench.py reports a kernel's traffic only "
+        "while the sha256 of the listed sources still matches.")
+    doc["sources"] = TRAFFIC_SOURCES
+    doc["copy_calibration"] = dict(copy_bytes=COPY_BYTES, fetch_kib=cf,
+                                   write_kib=cw,
+                                   fetch_factor=round(fetch_factor, 4),
+                                   write_factor=round(write_factor, 4))
+    doc.setdefault("kernels", {})
+    sha = _sources_sha256()
+    lines = ["| kernel | FETCH_SIZE KiB per dispatch | WRITE_SIZE KiB per "
+             "dispatch | scaled traffic per launch |", "|---|---|---|---|"]
+    for key, frag in TRAFFIC_KERNELS.items():
+        fk = [v for d, (n, v) in sorted(fetch.items()) if frag in n]
+        wk = [v for d, (n, v) in sorted(write.items()) if frag in n]
+        if not fk or not wk:
+            continue
+        traffic = int(round(sum(fk) / len(fk) * 1024 * fetch_factor +
+                            sum(wk) / len(wk) * 1024 * write_factor))
+        doc["kernels"]["%s/%s" % (workload, key)] = dict(
+            source_sha256=sha, fetch_kib=fk, write_kib=wk,
+            traffic_bytes_per_launch=traffic)
+        lines.append("| %s | %s | %s | %.3f GB |" % (
+            key, ", ".join("%.0f" % v for v in fk),
+            ", ".join("%.0f" % v for v in wk), traffic / 1e9))
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    print("Calibration: the %d-byte copy reads FETCH_SIZE = %.0f KiB and "
+          "WRITE_SIZE = %.0f KiB: fetch x %.4f, write x %.4f.\n" % (
+              COPY_BYTES, cf, cw, fetch_factor, write_factor))
+    print("\n".join(lines))
+
+
+def summarize_trace(trace_dir):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"),
+                      recursive=True)
+    print("| kernel | calls | total us | average us | min us | max us | % |")
+    print("|---|---|---|---|---|---|---|")
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Name"].replace("(anonymous namespace)::", "")
+                name = name.replace("void ", "").split("(")[0]
+                print("| %s | %s | %.1f | %.1f | %.1f | %.1f | %.1f |" % (
+                    name, r["Calls"], float(r["TotalDurationNs"]) / 1e3,
+                    float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                    float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+
+
 def recorded_traffic(key):
     """HBM bytes per launch recorded in profiles/traffic.json for `key`, if
     the kernel sources still hash to what they were when the counters were
     taken; None otherwise (the kernel has changed since)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             doc = json.load(f)
         rec = doc["kernels"][key]
-        h = hashlib.sha256()
-        for src in doc["sources"]:
-            with open(os.path.join(ROOT, src), "rb") as f:
-                h.update(f.read())
+        if doc["sources"] != TRAFFIC_SOURCES:
+            return None
+        sha = _sources_sha256()
     except (OSError, KeyError, ValueError):
         return None
-    if h.hexdigest() != rec["source_sha256"]:
+    if sha != rec["source_sha256"]:
         return None
     return rec["traffic_bytes_per_launch"]
 
@@ -151,6 +270,12 @@ def cpu_baseline(wl):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
