@@ -46,14 +46,19 @@ def build(verbose=True):
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950"] + objs + [
         "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    # every symbol must resolve: a kernel whose host stub went missing
-    # shows up here rather than at the first call
-    import ctypes
-    ctypes.CDLL(tmp)
-    os.replace(tmp, OUT)
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd),
+                                                         r.stderr))
+        # every symbol must resolve: a kernel whose host stub went missing
+        # shows up here rather than at the first call
+        import ctypes
+        ctypes.CDLL(tmp)
+        os.replace(tmp, OUT)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
     if verbose:
         print("built", OUT)
     return OUT
