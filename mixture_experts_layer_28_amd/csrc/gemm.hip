@@ -37,10 +37,14 @@
 
 #include "gemm_common.h"
 
+#ifndef MOE_DECODE_NT
+#define MOE_DECODE_NT true
+#endif
+
 namespace moe {
 namespace {
 
-template <int D, int BM, int BN, int WGM, bool GATEUP>
+template <int D, int BM, int BN, int WGM, bool GATEUP, bool NTW>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const typename Storage<D>::T* __restrict__ A,
     const typename Storage<D>::T* __restrict__ B0,
@@ -111,8 +115,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     for (int it = 0; it < CA; ++it)
       ra[it] = (k0 + ka[it] < K) ? *(const u32x4*)(pa[it] + k0) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int it = 0; it < CB; ++it)
-      rb[it] = (k0 + kb[it] < K) ? *(const u32x4*)(pb[it] + k0) : u32x4{0, 0, 0, 0};
+    for (int it = 0; it < CB; ++it) {
+      const u32x4* src = (const u32x4*)(pb[it] + k0);
+      rb[it] = (k0 + kb[it] < K) ? (NTW ? __builtin_nontemporal_load(src) : *src)
+                                 : u32x4{0, 0, 0, 0};
+    }
   };
   auto store = [&](int st) {
 #pragma unroll
@@ -308,7 +315,9 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
   }
 }
 
-template <int D, int BM, int BN, int WGM>
+// NTW: every weight element is read by one tile only (decode-sized
+// segments), so the weight tiles are streamed with nontemporal loads.
+template <int D, int BM, int BN, int WGM, bool NTW>
 hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                             int E, const void* wg, const void* wu,
                             const void* wd, const uint32_t* offsets,
@@ -317,7 +326,7 @@ hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
   {
     const uint32_t ncol = cdiv(I, BN / 2);
     const uint32_t grid = tile_grid(ncol * (cdiv(N, BM) + (uint32_t)E));
-    hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, true>), dim3(grid),
+    hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, true, NTW>), dim3(grid),
                        dim3(256), 0, st, (const S*)xd, (const S*)wg,
                        (const S*)wu, (S*)act, offsets, N, (int)H, (int)I, E,
                        ncol, E);
@@ -327,7 +336,7 @@ hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
   timing_mark(5, st);
   const uint32_t ncol = cdiv(H, BN);
   const uint32_t grid = tile_grid(ncol * (cdiv(N, BM) + (uint32_t)E + 1));
-  hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, false>), dim3(grid),
+  hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, false, NTW>), dim3(grid),
                      dim3(256), 0, st, (const S*)act, (const S*)wd,
                      (const S*)wd, (S*)y, offsets, N, (int)I, (int)H, E,
                      ncol, E + 1);
@@ -366,7 +375,7 @@ hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
                           void* y, hipStream_t st) {
   // Few rows per expert (decode): short row blocks waste less work.
   if (N < 96 * (int64_t)E)
-    return launch_mfma_pair<D, 32, 128, 1>(xd, N, H, I, E, wg, wu, wd,
+    return launch_mfma_pair<D, 32, 128, 1, MOE_DECODE_NT>(xd, N, H, I, E, wg, wu, wd,
                                            offsets, act, y, st);
   // Prefill: 256 x 256 tiles when every buffer range fits 31 bits.
   const int64_t lim = (int64_t)1 << 31;
@@ -374,7 +383,7 @@ hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
     return launch_experts_big(xd, D, N, H, I, E, wg, wu, wd, offsets, act, y,
                               st);
   }
-  return launch_mfma_pair<D, 128, 128, 2>(xd, N, H, I, E, wg, wu, wd,
+  return launch_mfma_pair<D, 128, 128, 2, false>(xd, N, H, I, E, wg, wu, wd,
                                           offsets, act, y, st);
 }
 
