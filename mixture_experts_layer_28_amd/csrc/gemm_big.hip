@@ -131,13 +131,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     }
   };
 
-  // ---- fragments and MFMAs ----------------------------------------------------
-  f32x4 acc[kFM][FN];
-#pragma unroll
-  for (int i = 0; i < kFM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  // ---- fragments, MFMAs and the epilogue ---------------------------------------
   auto brow = [&](int j) -> int {
     if (GATEUP) {
       constexpr int H2 = FN / 2;
@@ -149,9 +143,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   };
 
   const int nk = (K + kBK - 1) / kBK;
-  // The K loop for a wave with FMC MFMA row tiles (0: it only loads).
+  // The K loop and epilogue of a wave with FMC MFMA row tiles (0: it only
+  // loads).  Each count has its own accumulators, so a wave with fewer row
+  // tiles holds no idle accumulator registers.
   auto kloop = [&](auto fm_c) {
     constexpr int FMC = decltype(fm_c)::value;
+    constexpr int FA = FMC > 0 ? FMC : 1;
+    f32x4 acc[FA][FN];
+#pragma unroll
+    for (int i = 0; i < FA; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto read_frags = [&](int st, int half, V* fa, V* fb) {
       const S* As = sm + st * kStage;
       const S* Bs = As + kBM * kBK;
@@ -193,7 +195,36 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         if (kt + 2 < nk) dma((kt + 2) * kBK, st);
       }
     }
+
+#pragma unroll
+    for (int i = 0; i < FMC; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t r = row0 + tr0 + i * 16 + (lane >> 4) * 4 + q;
+        if (r >= tend) continue;
+        S* crow = C + r * NB;
+        if (GATEUP) {
+          constexpr int H2 = FN / 2;
+#pragma unroll
+          for (int j = 0; j < H2; ++j) {
+            const int64_t c = n0 + wn * (TN / 2) + j * 16 + (lane & 15);
+            if (c < NB) {
+              const float g = to_f32<D>(from_f32<D>(acc[i][j][q]));
+              const float u = to_f32<D>(from_f32<D>(acc[i][j + H2][q]));
+              crow[c] = from_f32<D>(silu_mul(g, u));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t c = n0 + wn * TN + j * 16 + (lane & 15);
+            if (c < NB) crow[c] = from_f32<D>(acc[i][j][q]);
+          }
+        }
+      }
+    }
   };
+  static_assert(kFM == 5, "the cases below cover 0..kFM row tiles");
   switch (fm) {
     case 5: kloop(std::integral_constant<int, 5>{}); break;
     case 4: kloop(std::integral_constant<int, 4>{}); break;
@@ -201,36 +232,6 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     case 2: kloop(std::integral_constant<int, 2>{}); break;
     case 1: kloop(std::integral_constant<int, 1>{}); break;
     default: kloop(std::integral_constant<int, 0>{}); break;
-  }
-
-  // ---- epilogue ---------------------------------------------------------------
-#pragma unroll
-  for (int i = 0; i < kFM; ++i) {
-    if (i >= fm) break;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t r = row0 + tr0 + i * 16 + (lane >> 4) * 4 + q;
-      if (r >= tend) continue;
-      S* crow = C + r * NB;
-      if (GATEUP) {
-        constexpr int H2 = FN / 2;
-#pragma unroll
-        for (int j = 0; j < H2; ++j) {
-          const int64_t c = n0 + wn * (TN / 2) + j * 16 + (lane & 15);
-          if (c < NB) {
-            const float g = to_f32<D>(from_f32<D>(acc[i][j][q]));
-            const float u = to_f32<D>(from_f32<D>(acc[i][j + H2][q]));
-            crow[c] = from_f32<D>(silu_mul(g, u));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t c = n0 + wn * TN + j * 16 + (lane & 15);
-          if (c < NB) crow[c] = from_f32<D>(acc[i][j][q]);
-        }
-      }
-    }
   }
 }
 
