@@ -86,6 +86,29 @@ def test_experts_stage(T, H, I, E, k, fmt, skew):
     assert_close(y_gpu, y_ref, fmt, "experts %s" % ((T, H, I, E, k, fmt),))
 
 
+@pytest.mark.parametrize("R", [321, 639, 641, 1065, 1281])
+def test_balanced_row_blocks(R):
+    """A prefill segment of R rows is cut into ceil(R / 320) row blocks of
+    equal size (floor/ceil of R / blocks); sizes just past a multiple of the
+    block limit, and 1065 rows (17 MFMA row tiles per block, shared 5-4-4-4
+    over the wave rows), must compute every row exactly once."""
+    rng = np.random.default_rng(R)
+    fmt, H, I, E = "bf16", 128, 192, 2
+    T = R + 150
+    x = round_to(rng.standard_normal((T, H)), fmt)
+    wg = round_to(rng.standard_normal((E, I, H)) / np.sqrt(H), fmt)
+    wu = round_to(rng.standard_normal((E, I, H)) / np.sqrt(H), fmt)
+    wd = round_to(rng.standard_normal((E, H, I)) / np.sqrt(I), fmt)
+    idx = np.zeros((T, 1), dtype=np.uint32)
+    idx[R:] = 1
+    idx = idx[rng.permutation(T)]
+    d = dispatch(x, idx, E)
+    assert d["offsets"][1] == R
+    y_ref = experts(d["xd"], d["offsets"], wg, wu, wd, fmt)
+    y_gpu = _experts_gpu(d, wg, wu, wd, fmt)
+    assert_close(y_gpu, y_ref, fmt, "balanced blocks R=%d" % R)
+
+
 def test_experts_zero_rows_for_trailing_segment():
     rng = np.random.default_rng(1)
     fmt = "bf16"

@@ -116,3 +116,36 @@ def test_full_size_sampled_tokens(name, T, ntok):
                                tokens)
     got = values(out[torch.tensor(tokens, device="cuda")])
     assert_close(got, ref, fmt, "%s T=%d" % (name, T))
+
+
+def test_timing_events_bracket_each_kernel():
+    """moe_set_timing_events: while set, a forward records its 8 events
+    around its 7 kernels on its own stream; the per-kernel intervals add up
+    to the whole, and switching recording off leaves later calls alone."""
+    import ctypes
+    from mixture_experts_layer_28_amd import _lib
+    wl = workloads.make("edge", device="cuda", k=4)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    stream = torch.cuda.current_stream()
+    for ev in evs:
+        ev.record(stream)  # materialise the handles
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * 8)(*[ev.cuda_event for ev in evs])
+    L = _lib.lib()
+    _lib.check(L.moe_set_timing_events(handles, 8))
+    try:
+        out = moe.moe_forward(wl["x"], wl["logits"], wl["w_gate"], wl["w_up"],
+                              wl["w_down"], 4, True)
+    finally:
+        _lib.check(L.moe_set_timing_events(None, 0))
+    torch.cuda.synchronize()
+    parts = [evs[i].elapsed_time(evs[i + 1]) for i in range(7)]
+    assert all(p >= 0.0 for p in parts), parts
+    whole = evs[0].elapsed_time(evs[7])
+    assert abs(sum(parts) - whole) <= 1e-3 + 1e-3 * whole, (parts, whole)
+    # recording off: the events keep their times
+    out2 = moe.moe_forward(wl["x"], wl["logits"], wl["w_gate"], wl["w_up"],
+                           wl["w_down"], 4, True)
+    torch.cuda.synchronize()
+    assert evs[0].elapsed_time(evs[7]) == whole
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
