@@ -57,6 +57,11 @@ def parse():
                         "workload) and COPY_DIR/{fetch,write} (the copy "
                         "calibration), update profiles/traffic.json and print "
                         "a markdown table")
+    p.add_argument("--route-sweep", action="store_true",
+                   help="extension, not the benchmark: time moe_route alone "
+                        "at T = 2^16, 2^18, 2^20 (bf16 logits, E and k as "
+                        "listed in ROUTE_SWEEP) with the Infinity Cache "
+                        "flushed before each call; one JSON line per case")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU work: print the kernel statistics of a "
                         "rocprofv3 --kernel-trace --stats run as markdown")
@@ -198,6 +203,46 @@ def record_traffic(workload, prof_dir, copy_dir):
     print("\n".join(lines))
 
 
+ROUTE_SWEEP = [(8, 2), (64, 8), (128, 8), (256, 8)]  # (E, top_k)
+
+
+def route_sweep():
+    """Streaming efficiency of the route kernel on its own at large T (the
+    benchmark workloads hold at most 1.5 MB of logits, far below where HBM
+    bandwidth decides).  Bytes: T*E logits read + T*k*(4 + 2) written."""
+    import statistics
+    import torch
+    import mixture_experts_layer_28_amd as moe
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for E, k in ROUTE_SWEEP:
+        for T in (1 << 16, 1 << 18, 1 << 20):
+            lg = torch.randn(T, E, device="cuda", generator=gen).to(
+                torch.bfloat16)
+            idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+            w = torch.empty(T, k, dtype=torch.bfloat16, device="cuda")
+            moe.moe_route(lg, k, True, idx, w)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(7):
+                flush.fill_(1)  # evicts the 256 MB Infinity Cache
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                moe.moe_route(lg, k, True, idx, w)
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            ms = statistics.median(ts)
+            nbytes = T * E * 2 + T * k * 6
+            print(json.dumps({"extension": "route_sweep", "E": E, "top_k": k,
+                              "T": T, "us": round(ms * 1e3, 1),
+                              "GB/s": round(nbytes / ms / 1e6, 1),
+                              "hbm_frac": round(nbytes / ms / 1e6 /
+                                                PEAK_HBM_GBS, 4)}),
+                  flush=True)
+
+
 def summarize_trace(trace_dir):
     """Markdown table of a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -275,6 +320,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.route_sweep:
+        route_sweep()
         return
     if args.copy_calibration:
         copy_calibration()

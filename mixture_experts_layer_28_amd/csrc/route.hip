@@ -11,13 +11,14 @@
 // softmax is strictly increasing in the logit, so this is the exact order of
 // the softmax values, and it is decided on exact data (no exp rounding).
 //
-// Layout: a group of G lanes (G = 8..64, a power of two >= min(E, 64))
-// owns one row; lane l of the group holds experts l, l+G, l+2G, ... in
-// registers.  Reductions are butterfly shuffles inside the group, so every
-// lane ends with the same bits.  Top-k takes k rounds; round j finds the
-// largest (logit, -id) key strictly below the key chosen in round j-1, so no
-// per-expert "taken" flags are needed.  Slot j's id and probability are kept
-// by lane j % G, which writes them at the end (coalesced).
+// Layout: a group of G lanes (a power of two, G * PL >= E with PL = 8, or 16
+// for E > 512; G = 1 for E <= 8) owns one row; lane l of the group holds the
+// PL consecutive experts l*PL .. l*PL+PL-1 in registers, read with 16-byte
+// loads where the row layout allows.  Reductions are butterfly shuffles
+// inside the group, so every lane ends with the same bits.  Top-k takes k
+// rounds; round j finds the largest (logit, -id) key strictly below the key
+// chosen in round j-1, so no per-expert "taken" flags are needed.  Slot j's
+// id and probability are kept by lane j % G, which writes them at the end.
 //
 // Rows with E > 1024 use a one-wave-per-row variant that re-reads the row
 // from memory each round instead of caching it.
@@ -28,38 +29,60 @@
 namespace moe {
 namespace {
 
+// Butterfly reductions inside a group of G lanes (a power of two, at most
+// 64, groups aligned to G lanes).  Steps within a 16-lane row use DPP lane
+// moves (quad permutes, then the half-row and row mirrors: after the quad
+// steps every lane of a quad holds the same value, so pairing quad q with
+// its mirror image combines distinct quads); wider steps use a permute.
+// Every lane of the group ends with the same bits (the combining operations
+// are commutative).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int G, typename F>
+__device__ __forceinline__ uint32_t group_reduce(uint32_t v, F op) {
+  if constexpr (G >= 2) v = op(v, dpp<0xB1>(v));    // quad_perm 1,0,3,2
+  if constexpr (G >= 4) v = op(v, dpp<0x4E>(v));    // quad_perm 2,3,0,1
+  if constexpr (G >= 8) v = op(v, dpp<0x141>(v));   // row_half_mirror
+  if constexpr (G >= 16) v = op(v, dpp<0x140>(v));  // row_mirror
+  if constexpr (G >= 32) v = op(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  if constexpr (G >= 64) v = op(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+  return v;
+}
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, G));
-  return v;
+  return __uint_as_float(group_reduce<G>(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, G);
-  return v;
+  return __uint_as_float(group_reduce<G>(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 template <int G>
 __device__ __forceinline__ int group_or(int v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o, G);
-  return v;
+  return (int)group_reduce<G>((uint32_t)v, [](uint32_t a, uint32_t b) { return a | b; });
 }
 template <int G>
 __device__ __forceinline__ int group_and(int v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v &= __shfl_xor(v, o, G);
-  return v;
+  return (int)group_reduce<G>((uint32_t)v, [](uint32_t a, uint32_t b) { return a & b; });
 }
 template <int G>
 __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  auto pair = [](uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; };
+  if constexpr (G >= 2) v = mx(v, pair(dpp<0xB1>((uint32_t)v), dpp<0xB1>((uint32_t)(v >> 32))));
+  if constexpr (G >= 4) v = mx(v, pair(dpp<0x4E>((uint32_t)v), dpp<0x4E>((uint32_t)(v >> 32))));
+  if constexpr (G >= 8) v = mx(v, pair(dpp<0x141>((uint32_t)v), dpp<0x141>((uint32_t)(v >> 32))));
+  if constexpr (G >= 16) v = mx(v, pair(dpp<0x140>((uint32_t)v), dpp<0x140>((uint32_t)(v >> 32))));
 #pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, G);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, G);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
+  for (int o = 16; o < G; o <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    v = mx(v, pair(lo, hi));
   }
   return v;
 }
@@ -68,8 +91,9 @@ __device__ __forceinline__ uint64_t make_key(float v, uint32_t e) {
   return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(0xffffffffu - e);
 }
 
-// Register-cached path: E <= G * PL <= 1024.
-template <int LDT, int G, int PL>
+// Register-cached path: E <= G * PL <= 1024.  VEC: every lane's PL values
+// are one or more aligned 16-byte vectors of the row.
+template <int LDT, int G, int PL, bool VEC>
 __global__ __launch_bounds__(256) void route_kernel(
     const typename Storage<LDT>::T* __restrict__ logits, int64_t T, int E,
     int k, int renorm, uint32_t* __restrict__ idx,
@@ -78,16 +102,29 @@ __global__ __launch_bounds__(256) void route_kernel(
   const int lane = threadIdx.x % G;
   const int64_t row = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
   if (row >= T) return;  // uniform across the group
-  const S* src = logits + row * (int64_t)E;
+  const S* src = logits + row * (int64_t)E + lane * PL;
+  const int e0 = lane * PL;
 
   float v[PL];
+  if constexpr (VEC) {
+    constexpr int NE = 16 / sizeof(S);  // elements per 16-byte vector
+    static_assert(PL % NE == 0, "whole vectors per lane");
+#pragma unroll
+    for (int q = 0; q < PL / NE; ++q) {
+      S tmp[NE];
+      *(u32x4*)tmp = *(const u32x4*)(src + q * NE);
+#pragma unroll
+      for (int i = 0; i < NE; ++i) v[q * NE + i] = to_f32<LDT>(tmp[i]);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < PL; ++m)
+      v[m] = e0 + m < E ? to_f32<LDT>(src[m]) : -INFINITY;
+  }
   int bad = 0, all_ninf = 1;
 #pragma unroll
   for (int m = 0; m < PL; ++m) {
-    const int e = lane + G * m;
-    v[m] = -INFINITY;
-    if (e < E) {
-      v[m] = to_f32<LDT>(src[e]);
+    if (e0 + m < E) {
       bad |= (__builtin_isnan(v[m]) || v[m] == INFINITY);
       all_ninf &= (v[m] == -INFINITY);
     }
@@ -107,47 +144,57 @@ __global__ __launch_bounds__(256) void route_kernel(
   float mx = -INFINITY;
 #pragma unroll
   for (int m = 0; m < PL; ++m)
-    if (lane + G * m < E) mx = fmaxf(mx, v[m]);
+    if (e0 + m < E) mx = fmaxf(mx, v[m]);
   mx = group_max<G>(mx);
   float s = 0.0f;
 #pragma unroll
   for (int m = 0; m < PL; ++m)
-    if (lane + G * m < E) s += expf(v[m] - mx);
+    if (e0 + m < E) s += expf(v[m] - mx);
   s = group_sum<G>(s);
 
-  float pj[PL];
-  uint32_t ej[PL];
+  // ranking keys, computed once; padding slots get key 0 (never chosen:
+  // a real key has ordered bits >= 1 or a nonzero id part)
+  uint64_t key[PL];
 #pragma unroll
-  for (int m = 0; m < PL; ++m) { pj[m] = 0.0f; ej[m] = 0u; }
+  for (int m = 0; m < PL; ++m)
+    key[m] = e0 + m < E ? make_key(v[m], (uint32_t)(e0 + m)) : 0ull;
+
+  // k rounds pick the keys; lane j % G keeps slot j's key and, after the
+  // rounds, turns it into an id and a probability (one exp per slot).
+  uint64_t kj[PL];
+#pragma unroll
+  for (int m = 0; m < PL; ++m) kj[m] = 0ull;
   uint64_t prev = ~0ull;
-  float den = 0.0f;
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int m = 0; m < PL; ++m) {
-      const int e = lane + G * m;
-      if (e < E) {
-        const uint64_t key = make_key(v[m], (uint32_t)e);
-        if (key < prev && key > best) best = key;
-      }
-    }
+    for (int m = 0; m < PL; ++m)
+      if (key[m] < prev && key[m] > best) best = key[m];
     best = group_max_u64<G>(best);
     prev = best;
-    const uint32_t eb = 0xffffffffu - (uint32_t)best;
-    const float vb = from_ordered_bits((uint32_t)(best >> 32));
-    const float p = expf(vb - mx) / s;
-    den += p;  // slot order, identical on every lane
     if (lane == (j % G)) {
 #pragma unroll
       for (int m = 0; m < PL; ++m)
-        if (m == j / G) { pj[m] = p; ej[m] = eb; }
+        if (m == j / G) kj[m] = best;
     }
   }
+  float pj[PL];
+  float part = 0.0f;  // this lane's slots, in slot order
+#pragma unroll
+  for (int m = 0; m < PL; ++m) {
+    pj[m] = 0.0f;
+    if (lane + G * m < k) {
+      const float vb = from_ordered_bits((uint32_t)(kj[m] >> 32));
+      pj[m] = expf(vb - mx) / s;
+      part += pj[m];
+    }
+  }
+  const float den = renorm ? group_sum<G>(part) : 1.0f;
 #pragma unroll
   for (int m = 0; m < PL; ++m) {
     const int j = lane + G * m;
     if (j < k) {
-      idx_row[j] = ej[m];
+      idx_row[j] = 0xffffffffu - (uint32_t)kj[m];
       w_row[j] = from_f32<LDT>(renorm ? pj[m] / den : pj[m]);
     }
   }
@@ -221,8 +268,15 @@ hipError_t launch_g(const void* logits, int64_t T, int E, int k, int renorm,
   using S = typename Storage<LDT>::T;
   const int rows = 256 / G;
   const dim3 grid((unsigned)((T + rows - 1) / rows));
-  hipLaunchKernelGGL((route_kernel<LDT, G, PL>), grid, dim3(256), 0, st,
-                     (const S*)logits, T, E, k, renorm, idx, (S*)w);
+  // 16-byte loads when every lane's PL values are whole aligned vectors
+  const bool vec = (PL * sizeof(S)) % 16 == 0 && E == G * PL &&
+                   (uintptr_t)logits % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL((route_kernel<LDT, G, PL, true>), grid, dim3(256), 0,
+                       st, (const S*)logits, T, E, k, renorm, idx, (S*)w);
+  else
+    hipLaunchKernelGGL((route_kernel<LDT, G, PL, false>), grid, dim3(256), 0,
+                       st, (const S*)logits, T, E, k, renorm, idx, (S*)w);
   return hipGetLastError();
 }
 
@@ -230,12 +284,12 @@ template <int LDT>
 hipError_t launch_route_t(const void* logits, int64_t T, int E, int k,
                           int renorm, uint32_t* idx, void* w, hipStream_t st) {
   using S = typename Storage<LDT>::T;
-  if (E <= 8) return launch_g<LDT, 8, 1>(logits, T, E, k, renorm, idx, w, st);
-  if (E <= 16) return launch_g<LDT, 16, 1>(logits, T, E, k, renorm, idx, w, st);
-  if (E <= 32) return launch_g<LDT, 32, 1>(logits, T, E, k, renorm, idx, w, st);
-  if (E <= 64) return launch_g<LDT, 64, 1>(logits, T, E, k, renorm, idx, w, st);
-  if (E <= 128) return launch_g<LDT, 64, 2>(logits, T, E, k, renorm, idx, w, st);
-  if (E <= 256) return launch_g<LDT, 64, 4>(logits, T, E, k, renorm, idx, w, st);
+  if (E <= 8) return launch_g<LDT, 1, 8>(logits, T, E, k, renorm, idx, w, st);
+  if (E <= 16) return launch_g<LDT, 2, 8>(logits, T, E, k, renorm, idx, w, st);
+  if (E <= 32) return launch_g<LDT, 4, 8>(logits, T, E, k, renorm, idx, w, st);
+  if (E <= 64) return launch_g<LDT, 8, 8>(logits, T, E, k, renorm, idx, w, st);
+  if (E <= 128) return launch_g<LDT, 16, 8>(logits, T, E, k, renorm, idx, w, st);
+  if (E <= 256) return launch_g<LDT, 32, 8>(logits, T, E, k, renorm, idx, w, st);
   if (E <= 512) return launch_g<LDT, 64, 8>(logits, T, E, k, renorm, idx, w, st);
   if (E <= 1024) return launch_g<LDT, 64, 16>(logits, T, E, k, renorm, idx, w, st);
   const dim3 grid((unsigned)((T + 3) / 4));
