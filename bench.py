@@ -10,7 +10,8 @@ device synchronisation; one JSON line on stdout.
 
 Per-kernel durations come from HIP events the library records around each of
 its kernels on the forward's stream (moe_set_timing_events), averaged over
-the K timed steps.  The roofline object describes the dominant kernel (the
+the K timed steps; step_gpu_ms gives the median and minimum GPU time of one
+step (first kernel start to last kernel end).  The roofline object describes the dominant kernel (the
 gate+up grouped GEMM with the SwiGLU epilogue).  The CPU baseline times the
 oracle (numpy) on a few tokens of the same workload.
 """
@@ -389,6 +390,8 @@ def main():
         for j, name in enumerate(KERNELS):
             per_kernel[name] += evs[j].elapsed_time(evs[j + 1])
     per_kernel = {n: v / args.steps for n, v in per_kernel.items()}  # ms
+    # GPU time of each step, first kernel start to last kernel end
+    step_gpu = sorted(evs[0].elapsed_time(evs[7]) for evs in marks)
 
     alg = algorithmic(wl, counts)
     stages = {}
@@ -431,6 +434,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_gpu_ms": {"p50": round(step_gpu[len(step_gpu) // 2], 4),
+                        "min": round(step_gpu[0], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
