@@ -74,7 +74,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     uint32_t* __restrict__ table, int64_t nchunks, int E,
     uint32_t* __restrict__ offsets) {
   __shared__ uint32_t run_sum[1024];
-  __shared__ uint32_t bin_base[1025];
+  __shared__ uint32_t bin_base[1024];  // bases of the bins of one pass
   __shared__ uint32_t carry;
   const int tid = threadIdx.x;
   const int nb = E + 1;
@@ -106,15 +106,15 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     if (tid == 0) {
       uint32_t acc = carry;
       for (int j = 0; j < bins_per_pass && pass * bins_per_pass + j < nb; ++j) {
-        bin_base[pass * bins_per_pass + j] = acc;
+        bin_base[j] = acc;
         acc += run_sum[j * P + P - 1];
       }
       carry = acc;
     }
     __syncthreads();
     if (b < nb) {
-      uint32_t run = bin_base[b] + run_sum[tid] - mine;
-      if (lp == 0) offsets[b] = bin_base[b];  // offsets[E] = first invalid row
+      uint32_t run = bin_base[bl] + run_sum[tid] - mine;
+      if (lp == 0) offsets[b] = bin_base[bl];  // offsets[E] = first invalid row
       for (int64_t c = c0; c < c1; ++c) {
         const uint32_t n = table[c * nb + b];
         table[c * nb + b] = run;

@@ -112,3 +112,17 @@ def test_full_size_workloads(name, T):
     g = _run(wl["x"], idx, E)
     ref = dispatch(np.zeros((T, 1)), idx, E)
     assert_dispatch_matches(g, ref, idx, E, x_bits=_bits(wl["x"]))
+
+
+def test_largest_expert_count():
+    """E = 16383, the largest the dispatch accepts (the count table of one
+    chunk fills the LDS scan), with most experts empty."""
+    rng = np.random.default_rng(11)
+    T, E, k = 300, 16383, 4
+    idx = _random_idx(rng, T, E, k, skew=True)
+    idx[0, 0] = E - 1
+    x = torch.from_numpy(rng.standard_normal((T, 24)).astype(np.float32)).to(
+        torch.bfloat16)
+    g = _run(x, idx, E)
+    ref = dispatch(np.zeros((T, 1)), idx, E)
+    assert_dispatch_matches(g, ref, idx, E, x_bits=_bits(x))

@@ -109,6 +109,23 @@ def test_balanced_row_blocks(R):
     assert_close(y_gpu, y_ref, fmt, "balanced blocks R=%d" % R)
 
 
+def test_largest_expert_count():
+    """E = 16383 experts (the library's limit), a few rows each for a
+    handful of them and none for the rest."""
+    rng = np.random.default_rng(12)
+    T, H, I, E, k, fmt = 64, 16, 24, 16383, 2, "bf16"
+    x = round_to(rng.standard_normal((T, H)), fmt)
+    idx = rng.choice([0, 1, 7, 5000, E - 1], size=(T, k)).astype(np.uint32)
+    idx[:, 1] = (idx[:, 0] + 1 + rng.integers(0, 3, size=T)) % E
+    wg = round_to(rng.standard_normal((E, I, H)) / 4.0, fmt)
+    wu = round_to(rng.standard_normal((E, I, H)) / 4.0, fmt)
+    wd = round_to(rng.standard_normal((E, H, I)) / 5.0, fmt)
+    d = dispatch(x, idx, E)
+    y_ref = experts(d["xd"], d["offsets"], wg, wu, wd, fmt)
+    y_gpu = _experts_gpu(d, wg, wu, wd, fmt)
+    assert_close(y_gpu, y_ref, fmt, "E=16383")
+
+
 def test_experts_zero_rows_for_trailing_segment():
     rng = np.random.default_rng(1)
     fmt = "bf16"

@@ -111,3 +111,16 @@ def test_full_size_workloads(name, T):
     if name == "fine":
         counts = np.bincount(idx.ravel().astype(np.int64), minlength=64)
         assert (counts == 0).any()  # the bias leaves some experts idle
+
+
+@pytest.mark.parametrize("k", [1, 8, 64])
+def test_largest_expert_count(k):
+    """E = 65536, the largest the library accepts (one wave per row,
+    values re-read each round), with ties and a row holding -inf."""
+    rng = np.random.default_rng(k)
+    E, T = 65536, 3
+    lg = (rng.integers(-40, 41, size=(T, E)) * 0.25).astype(np.float32)
+    lg[1, ::3] = -np.inf
+    for fmt in ("f32", "bf16"):
+        _check(torch.from_numpy(lg).to(TDT[fmt]), k, True,
+               "E=65536 k=%d %s" % (k, fmt))
