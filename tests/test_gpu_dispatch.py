@@ -56,6 +56,7 @@ def _run(x, idx, E):
     (700, 7, 5, 3, torch.float16, False),      # odd H: 2-byte copies
     (300, 6, 200, 8, torch.float32, True),     # more experts than fit a wave
     (2049, 16, 1024, 2, torch.bfloat16, True),
+    (20000, 8, 4000, 8, torch.bfloat16, True),  # grown chunks, 4 count waves
 ])
 def test_random(T, H, E, k, dtype, skew):
     rng = np.random.default_rng(T + E)

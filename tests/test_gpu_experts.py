@@ -74,6 +74,8 @@ SHAPES = [
     (20, 512, 384, 64, 8, "bf16", False),    # ~2.5 rows per expert (decode)
     (130, 100, 60, 6, 2, "bf16", False),     # K % 8 != 0: generic path
     (97, 256, 128, 1, 1, "bf16", False),     # a single expert
+    (400, 8, 16, 4, 1, "bf16", False),       # prefill tiles, K = 8 and 16:
+    (600, 24, 40, 4, 1, "f16", True),        #   one partial K stage
 ]
 
 

@@ -59,7 +59,8 @@ def test_edge_workload(k, renorm):
 
 @pytest.mark.parametrize("T,H,I,E,k,renorm", [
     (45, 136, 200, 5, 2, True), (260, 64, 96, 12, 3, False),
-    (1, 32, 16, 4, 4, True), (129, 128, 128, 2, 1, False)])
+    (1, 32, 16, 4, 4, True), (129, 128, 128, 2, 1, False),
+    (300, 32, 24, 2000, 4, True)])   # E > 1024: wide route, multi-pass scan
 def test_ragged_shapes(T, H, I, E, k, renorm):
     wl = workloads.make("edge", T=T, H=H, I=I, E=E, k=k)
     for name in ("x", "logits", "w_gate", "w_up", "w_down"):
