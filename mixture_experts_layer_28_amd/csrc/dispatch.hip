@@ -75,6 +75,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     uint32_t* __restrict__ offsets) {
   __shared__ uint32_t run_sum[1024];
   __shared__ uint32_t bin_base[1024];  // bases of the bins of one pass
+  __shared__ uint32_t wave_base[16], pass_total;
   __shared__ uint32_t carry;
   const int tid = threadIdx.x;
   const int nb = E + 1;
@@ -89,9 +90,23 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   if (tid == 0) carry = 0;
   for (int pass = 0; pass * bins_per_pass < nb; ++pass) {
     const int b = pass * bins_per_pass + bl;
+    // a run of up to kRun chunks stays in registers between the two walks
+    // (all its loads in flight at once); longer runs are read twice
+    constexpr int kRun = 32;
+    const bool cached = c1 - c0 <= kRun;
+    uint32_t cv[kRun];
     uint32_t mine = 0;
-    if (b < nb)
-      for (int64_t c = c0; c < c1; ++c) mine += table[c * nb + b];
+    if (b < nb) {
+      if (cached) {
+#pragma unroll
+        for (int i = 0; i < kRun; ++i)
+          cv[i] = c0 + i < c1 ? table[(c0 + i) * nb + b] : 0u;
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) mine += cv[i];
+      } else {
+        for (int64_t c = c0; c < c1; ++c) mine += table[c * nb + b];
+      }
+    }
     run_sum[tid] = mine;
     __syncthreads();
     // inclusive scan of the P run sums of each bin (Hillis-Steele)
@@ -101,24 +116,51 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
       run_sum[tid] += add;
       __syncthreads();
     }
-    // bin totals of this pass -> exclusive prefix over all bins (serial in
-    // one thread: at most 1024 adds per pass)
-    if (tid == 0) {
-      uint32_t acc = carry;
-      for (int j = 0; j < bins_per_pass && pass * bins_per_pass + j < nb; ++j) {
-        bin_base[j] = acc;
-        acc += run_sum[j * P + P - 1];
+    // bin totals of this pass -> exclusive prefix over the bins: thread j
+    // holds bin j's total; wave prefix sums, then one wave scans the 16
+    // wave sums
+    const int lane = tid & 63, wv = tid >> 6;
+    uint32_t tot = 0;
+    if (tid < bins_per_pass && pass * bins_per_pass + tid < nb)
+      tot = run_sum[tid * P + P - 1];
+    uint32_t inc = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wave_base[wv] = inc;
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t ws = tid < 16 ? wave_base[tid] : 0u;
+      uint32_t wi = ws;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const uint32_t y = __shfl_up(wi, o, 64);
+        if (tid >= o) wi += y;
       }
-      carry = acc;
+      if (tid < 16) wave_base[tid] = wi - ws;
+      if (tid == 15) pass_total = wi;
     }
     __syncthreads();
+    if (tid < bins_per_pass) bin_base[tid] = carry + wave_base[wv] + inc - tot;
+    __syncthreads();
+    if (tid == 0) carry += pass_total;  // next read after this pass ends
     if (b < nb) {
       uint32_t run = bin_base[bl] + run_sum[tid] - mine;
       if (lp == 0) offsets[b] = bin_base[bl];  // offsets[E] = first invalid row
-      for (int64_t c = c0; c < c1; ++c) {
-        const uint32_t n = table[c * nb + b];
-        table[c * nb + b] = run;
-        run += n;
+      if (cached) {
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) {
+          if (c0 + i < c1) table[(c0 + i) * nb + b] = run;
+          run += cv[i];
+        }
+      } else {
+        for (int64_t c = c0; c < c1; ++c) {
+          const uint32_t n = table[c * nb + b];
+          table[c * nb + b] = run;
+          run += n;
+        }
       }
     }
     __syncthreads();
