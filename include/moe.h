@@ -147,7 +147,9 @@ int moe_experts_forward(const void* xd, int dt, int64_t N, int64_t H,
  *
  * out[t] = sum over slots j = 0..top_k-1, in slot order and in FP32, of
  * weights[t,j] * y[token_row[t,j]], rounded once to dt.  The routing
- * weights are applied here and nowhere else.  token_row values must be < N.
+ * weights are applied here and nowhere else.  A token_row value >= N makes
+ * that token's output NaN instead of being read.  top_k <= 8192
+ * (MOE_ERR_UNSUPPORTED beyond).
  */
 int moe_combine(const void* y, int dt, int64_t N, int64_t T, int64_t H,
                 int64_t top_k, const void* weights, int wdt,
@@ -170,6 +172,10 @@ size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E,
  *   w_gate, w_up [E,I,H], w_down [E,H,I]   dt
  *   out    [T,H]   dt    output
  *   workspace  moe_forward_workspace_size(...) bytes, 256-byte aligned
+ *
+ * Limits are those of the four stages: 1 <= top_k <= E, E <= 16383,
+ * top_k <= 8192, T*top_k < 2^32.  The workspace holds the routing result,
+ * the dispatch mapping and rows, the dispatch count table, act and y.
  */
 int moe_forward(const void* x, int dt, const void* logits, int ldt,
                 int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,

@@ -58,6 +58,8 @@ bool bytes_ok(int64_t a, int64_t b, int64_t s) {
 constexpr int64_t kMaxRows = 0xffffffffLL;  // row ids are uint32
 constexpr int64_t kMaxRouteE = 65536;
 constexpr int64_t kMaxDispatchE = 16383;    // count table fits LDS
+constexpr int64_t kMaxCombineK = 8192;      // one token's row ids and weights
+                                            // fit 64 KB of LDS
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -121,7 +123,7 @@ int check_combine(const void* y, int dt, int64_t N, int64_t T, int64_t H,
   int64_t n;
   if (!mul_ok(T, k, &n) || n > kMaxRows || N > kMaxRows) return fail(MOE_ERR_SHAPE, "moe_combine: T*top_k and N must be < 2^32");
   if (!bytes_ok(N > T ? N : T, H, dsize(dt))) return fail(MOE_ERR_SHAPE, "moe_combine: size overflows");
-  if (k > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: top_k > 1024");
+  if (k > kMaxCombineK) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: top_k > %lld", (long long)kMaxCombineK);
   if (T > 0 && (!y || !w || !token_row || !out)) return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
   return MOE_OK;
 }
@@ -290,6 +292,7 @@ int moe_forward(const void* x, int dt, const void* logits, int ldt,
   s = check_experts(x, dt, T * top_k, H, I, E, w_gate, w_up, w_down, x, x, x);
   if (s != MOE_OK) return s;
   if (T > 0 && (!x || !out)) return fail(MOE_ERR_INVALID_ARG, "moe_forward: null pointer");
+  if (top_k > kMaxCombineK) return fail(MOE_ERR_UNSUPPORTED, "moe_forward: top_k > %lld", (long long)kMaxCombineK);
   const size_t need = moe_forward_workspace_size(T, H, I, E, top_k, dt, ldt);
   if (need == 0) return fail(MOE_ERR_SHAPE, "moe_forward: sizes out of range");
   if (!workspace || workspace_bytes < need)

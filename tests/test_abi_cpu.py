@@ -105,7 +105,7 @@ def test_combine_rejects():
     L = _lib.lib()
     base = [FAKE, 2, 20, 10, 16, 2, FAKE, 2, FAKE, FAKE, None]
     for i, v, st in [(1, 5, 3), (7, 5, 3), (5, 0, 1), (4, 0, 2),
-                     (8, None, 1), (5, 2000, 4)]:
+                     (8, None, 1), (5, 8193, 4)]:
         a = list(base)
         a[i] = v
         assert L.moe_combine(*a) == st, (i, v)
@@ -134,6 +134,9 @@ def test_forward_workspace_and_rejects():
     a = list(args)
     a[10] = None
     assert L.moe_forward(*a) == 1
+    a = list(args)
+    a[7], a[8] = 16383, 8193  # top_k beyond what combine stages in LDS
+    assert L.moe_forward(*a) == 4 and "top_k" in _last()
 
 
 def test_timing_events_rejects_wrong_counts():
