@@ -48,16 +48,56 @@ def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _out(t, shape, dtype, dev, what):
+    """A caller's output tensor must be exactly what the kernels write:
+    the library only sees a pointer, so a short or strided one would be
+    written out of bounds.  None allocates one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev
+            or not t.is_contiguous()):
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s"
+                         % (what, dtype, tuple(shape), dev))
+    return t
+
+
+def _index(t, shape, what):
+    """Index arrays are uint32 in the C ABI: int32 tensors here."""
+    if t.dtype != _U32 or tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be an int32 tensor of shape %s"
+                         % (what, tuple(shape)))
+    return t
+
+
+def _workspace(ws, need, dev):
+    """(tensor, bytes) of a scratch buffer of at least `need` bytes."""
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if ws.device != dev or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+    return ws, ws.numel() * ws.element_size()
+
+
+def _experts_weights(w_gate, w_up, w_down, H, dtype):
+    E, I, H2 = w_gate.shape
+    if H2 != H or tuple(w_up.shape) != (E, I, H) or tuple(
+            w_down.shape) != (E, H, I):
+        raise ValueError("expert weight shapes must be gate/up [E,I,H], "
+                         "down [E,H,I] with H matching the rows")
+    for w in (w_gate, w_up, w_down):
+        if w.dtype != dtype:
+            raise TypeError("expert weights and rows must share one dtype")
+    return E, I
+
+
 def moe_route(logits, top_k, renormalize=True, idx=None, weights=None):
     """Softmax/top-k routing.  logits [T,E] -> (idx int32 [T,k],
     weights [T,k] in the logits dtype)."""
     logits = _c(logits)
     dev = _dev(logits)
     T, E = logits.shape
-    if idx is None:
-        idx = torch.empty((T, top_k), dtype=_U32, device=dev)
-    if weights is None:
-        weights = torch.empty((T, top_k), dtype=logits.dtype, device=dev)
+    idx = _out(idx, (T, top_k), _U32, dev, "idx")
+    weights = _out(weights, (T, top_k), logits.dtype, dev, "weights")
     check(lib().moe_route(_p(logits), _dt(logits, "logits"), T, E, top_k,
                           int(bool(renormalize)), _p(idx), _p(weights),
                           _stream(dev)))
@@ -76,12 +116,10 @@ def moe_dispatch(x, idx, num_experts, workspace=None):
     dev = _dev(x, idx)
     T, H = x.shape
     k = idx.shape[1]
-    if idx.shape[0] != T:
-        raise ValueError("idx must be [T, top_k]")
+    _index(idx, (T, k), "idx")
     N = T * k
-    ws_bytes = moe_dispatch_workspace_size(T, num_experts, k)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(
+        workspace, moe_dispatch_workspace_size(T, num_experts, k), dev)
     out = dict(
         xd=torch.empty((N, H), dtype=x.dtype, device=dev),
         offsets=torch.empty(num_experts + 1, dtype=_U32, device=dev),
@@ -92,7 +130,7 @@ def moe_dispatch(x, idx, num_experts, workspace=None):
     check(lib().moe_dispatch(
         _p(x), _dt(x, "x"), T, H, num_experts, k, _p(idx), _p(out["xd"]),
         _p(out["offsets"]), _p(out["row_expert"]), _p(out["row_token"]),
-        _p(out["token_row"]), _p(workspace), workspace.numel(), _stream(dev)))
+        _p(out["token_row"]), _p(workspace), ws_bytes, _stream(dev)))
     return out
 
 
@@ -103,20 +141,10 @@ def moe_experts_forward(xd, offsets, w_gate, w_up, w_down, act=None, y=None):
     w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
     dev = _dev(xd, offsets, w_gate, w_up, w_down)
     N, H = xd.shape
-    E, I, H2 = w_gate.shape
-    if H2 != H or tuple(w_up.shape) != (E, I, H) or tuple(
-            w_down.shape) != (E, H, I):
-        raise ValueError("expert weight shapes must be gate/up [E,I,H], "
-                         "down [E,H,I] with H matching xd")
-    for w in (w_gate, w_up, w_down):
-        if w.dtype != xd.dtype:
-            raise TypeError("expert weights and rows must share one dtype")
-    if offsets.numel() != E + 1:
-        raise ValueError("offsets must have E+1 entries")
-    if act is None:
-        act = torch.empty((N, I), dtype=xd.dtype, device=dev)
-    if y is None:
-        y = torch.empty((N, H), dtype=xd.dtype, device=dev)
+    E, I = _experts_weights(w_gate, w_up, w_down, H, xd.dtype)
+    _index(offsets, (E + 1,), "offsets")
+    act = _out(act, (N, I), xd.dtype, dev, "act")
+    y = _out(y, (N, H), xd.dtype, dev, "y")
     check(lib().moe_experts_forward(
         _p(xd), _dt(xd, "xd"), N, H, I, E, _p(w_gate), _p(w_up), _p(w_down),
         _p(offsets), _p(act), _p(y), _stream(dev)))
@@ -130,8 +158,8 @@ def moe_combine(y, weights, token_row, out=None):
     dev = _dev(y, weights, token_row)
     N, H = y.shape
     T, k = weights.shape
-    if out is None:
-        out = torch.empty((T, H), dtype=y.dtype, device=dev)
+    _index(token_row, (T, k), "token_row")
+    out = _out(out, (T, H), y.dtype, dev, "out")
     check(lib().moe_combine(_p(y), _dt(y, "y"), N, T, H, k, _p(weights),
                             _dt(weights, "weights"), _p(token_row), _p(out),
                             _stream(dev)))
@@ -150,18 +178,18 @@ def moe_forward(x, logits, w_gate, w_up, w_down, top_k, renormalize=True,
     w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
     dev = _dev(x, logits, w_gate, w_up, w_down)
     T, H = x.shape
-    E, I, _ = w_gate.shape
+    E, I = _experts_weights(w_gate, w_up, w_down, H, x.dtype)
     if logits.shape != (T, E):
         raise ValueError("logits must be [T, E]")
-    ws = moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype)
-    if workspace is None:
-        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
-    if out is None:
-        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    workspace, ws_bytes = _workspace(
+        workspace,
+        moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype),
+        dev)
+    out = _out(out, (T, H), x.dtype, dev, "out")
     check(lib().moe_forward(
         _p(x), _dt(x, "x"), _p(logits), _dt(logits, "logits"), T, H, I, E,
         top_k, int(bool(renormalize)), _p(w_gate), _p(w_up), _p(w_down),
-        _p(out), _p(workspace), workspace.numel(), _stream(dev)))
+        _p(out), _p(workspace), ws_bytes, _stream(dev)))
     return out
 
 

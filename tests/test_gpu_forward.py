@@ -150,3 +150,39 @@ def test_timing_events_bracket_each_kernel():
     torch.cuda.synchronize()
     assert evs[0].elapsed_time(evs[7]) == whole
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks what the C ABI cannot see (it gets pointers and
+    sizes only): output shapes, dtypes and contiguity, weight shapes and
+    index dtypes, before anything is launched."""
+    wl = workloads.make("edge", device="cuda", k=2)
+    x, lg = wl["x"], wl["logits"]
+    wg, wu, wd = wl["w_gate"], wl["w_up"], wl["w_down"]
+    T, H = x.shape
+    E = lg.shape[1]
+    with pytest.raises(ValueError):
+        moe.moe_forward(x, lg, wg, wu, wd[:, :, :-8].contiguous(), 2)
+    with pytest.raises(TypeError):
+        moe.moe_forward(x, lg, wg, wu.to(torch.float32), wd, 2)
+    with pytest.raises(ValueError):
+        moe.moe_forward(x, lg, wg, wu, wd, 2, out=torch.empty_like(x)[:-1])
+    with pytest.raises(ValueError):
+        moe.moe_forward(x, lg, wg, wu, wd, 2,
+                        out=torch.empty((H, T), dtype=x.dtype,
+                                        device=x.device).t())
+    with pytest.raises(ValueError):
+        moe.moe_route(lg, 2, idx=torch.empty((T, 2), dtype=torch.int64,
+                                             device=lg.device))
+    idx, w = moe.moe_route(lg, 2)
+    with pytest.raises(ValueError):
+        moe.moe_dispatch(x, idx.to(torch.int64), E)
+    d = moe.moe_dispatch(x, idx, E)
+    with pytest.raises(ValueError):
+        moe.moe_experts_forward(d["xd"], d["offsets"], wg, wu, wd,
+                                y=torch.empty((T, H), dtype=x.dtype,
+                                              device=x.device))
+    y = moe.moe_experts_forward(d["xd"], d["offsets"], wg, wu, wd)
+    with pytest.raises(ValueError):
+        moe.moe_combine(y, w, d["token_row"][:, :1].contiguous())
+    torch.cuda.synchronize()
