@@ -25,6 +25,13 @@ Parity status of each function (what pins it is listed in the test files
                               brute-force loops)
 * ``moe.combine``             pinned (k=1 identity, brute force)
 * ``moe.forward``             pinned (brute force at T<=4, identical experts)
+* ``grouped.route_sigmoid_grouped``  pinned (golden cases, brute force by
+                              counting, sort reduction, scipy ``expit``)
+* ``grouped.forward_sigmoid_grouped`` pinned (per-token sum, identical
+                              experts)
+
+``grouped`` follows section 10 of the same guide (group-limited sigmoid
+routing) and the experts page's ``forward_sigmoid_grouped``.
 """
 
-from . import fp, moe  # noqa: F401
+from . import fp, grouped, moe  # noqa: F401
