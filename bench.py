@@ -3,9 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one moe_forward call (route -> dispatch -> SwiGLU experts ->
-combine) over one batch of synthetic inputs already resident in HBM.  The
-default workload is the Mixtral-shaped bf16 layer (T=4096, H=4096, I=14336,
-E=8, top-2, renormalised).  W untimed steps, then K timed steps bracketed by
+combine) over one batch of synthetic inputs already resident in HBM; for the
+``grouped`` workload, one moe_forward_sigmoid_grouped call (group-limited
+sigmoid routing in place of the softmax).  The default workload is the
+Mixtral-shaped bf16 layer (T=4096, H=4096, I=14336, E=8, top-2,
+renormalised).  W untimed steps, then K timed steps bracketed by
 device synchronisation; one JSON line on stdout.
 
 Per-kernel durations come from HIP events the library records around each of
@@ -37,6 +39,7 @@ WORKLOADS = {
     "fine": ("fine", None),
     "decode32": ("decode", 32),
     "decode256": ("decode", 256),
+    "grouped": ("grouped", None),
 }
 CPU_SAMPLE_MAX_TOKENS = 256
 CPU_SAMPLE_SECONDS = 15.0
@@ -98,7 +101,8 @@ def algorithmic(wl, counts):
     w_gu = 2 * touched * I * H * s
     w_d = touched * H * I * s
     return {
-        "route": dict(bytes=T * E * sl + N * (4 + sl)),
+        "route": dict(bytes=T * E * sl + N * (4 + sl)
+                      + (E * 4 if wl.get("bias") is not None else 0)),
         "dispatch_count": dict(bytes=N * 4 * 2),
         "dispatch_scan": dict(bytes=(E + 1) * 4),
         "dispatch_scatter": dict(bytes=T * H * s + N * H * s + N * 4 * 5),
@@ -290,19 +294,29 @@ def cpu_baseline(wl):
     from threadpoolctl import threadpool_info
 
     from mixture_experts_layer_28_amd import workloads
+    from oracle.grouped import forward_sigmoid_tokens
     from oracle.moe import forward_tokens
 
     fmt = wl["fmt"]
     host = {key: workloads.to_numpy(wl[key], fmt)
             for key in ("x", "logits", "w_gate", "w_up", "w_down")}
+    grouped = "groups" in wl
+    bias = wl["bias"].cpu().numpy() if wl.get("bias") is not None else None
     rng = np.random.default_rng(123)
     order = rng.permutation(wl["T"])[:CPU_SAMPLE_MAX_TOKENS].tolist()
     tokens = 0
     t0 = time.perf_counter()
     for t in order:
-        forward_tokens(host["x"], host["logits"], host["w_gate"],
-                       host["w_up"], host["w_down"], wl["k"], wl["renorm"],
-                       fmt, [t])
+        if grouped:
+            forward_sigmoid_tokens(
+                host["x"], host["logits"], bias, host["w_gate"],
+                host["w_up"], host["w_down"], wl["k"], wl["groups"],
+                wl["selected_groups"], wl["group_top_two"], wl["renorm"],
+                wl["scale"], fmt, [t])
+        else:
+            forward_tokens(host["x"], host["logits"], host["w_gate"],
+                           host["w_up"], host["w_down"], wl["k"],
+                           wl["renorm"], fmt, [t])
         tokens += 1
         if time.perf_counter() - t0 >= CPU_SAMPLE_SECONDS:
             break
@@ -347,8 +361,17 @@ def main():
     x, logits = wl["x"], wl["logits"]
     wg, wu, wd = wl["w_gate"], wl["w_up"], wl["w_down"]
 
+    grouped = base == "grouped"
+    if grouped:
+        gargs = (k, wl["groups"], wl["selected_groups"])
+        gopts = dict(bias=wl["bias"], group_top_two=wl["group_top_two"],
+                     renormalize=wl["renorm"], scale=wl["scale"])
+
     # routing histogram (outside the timed region): touched experts
-    idx, _ = moe.moe_route(logits, k, wl["renorm"])
+    if grouped:
+        idx, _ = moe.moe_route_sigmoid_grouped(logits, *gargs, **gopts)
+    else:
+        idx, _ = moe.moe_route(logits, k, wl["renorm"])
     d = moe.moe_dispatch(x, idx, E)
     off = d["offsets"].cpu().numpy().astype(np.int64)
     counts = np.diff(off)
@@ -359,8 +382,12 @@ def main():
     out = torch.empty((T, H), dtype=x.dtype, device=dev)
 
     def step():
-        moe.moe_forward(x, logits, wg, wu, wd, k, wl["renorm"], out=out,
-                        workspace=ws)
+        if grouped:
+            moe.moe_forward_sigmoid_grouped(x, logits, wg, wu, wd, *gargs,
+                                            out=out, workspace=ws, **gopts)
+        else:
+            moe.moe_forward(x, logits, wg, wu, wd, k, wl["renorm"], out=out,
+                            workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -442,8 +469,13 @@ def main():
         "dtype": "bf16" if wl["fmt"] == "bf16" else wl["fmt"],
         "data": "synthetic",
         "config": {"workload": "%s bf16 T=%d H=%d I=%d E=%d top_k=%d "
-                               "renormalize=%s" % (base, T, H, I, E, k,
-                                                   wl["renorm"]),
+                               "renormalize=%s%s" % (
+                                   base, T, H, I, E, k, wl["renorm"],
+                                   " sigmoid groups=%d selected=%d "
+                                   "top_two=%s scale=%g bias" % (
+                                       wl["groups"], wl["selected_groups"],
+                                       wl["group_top_two"], wl["scale"])
+                                   if grouped else ""),
                    "T": T, "H": H, "I": I, "E": E, "top_k": k,
                    "touched_experts": alg["touched_experts"],
                    "flop_per_step": 6 * T * k * H * I},

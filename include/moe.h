@@ -11,6 +11,9 @@
  *   logits [T,E] -> FP32 softmax over all E + top-k -> compact dispatch
  *   -> SwiGLU experts -> weighted combine -> out [T,H]
  *
+ * and the same pass with the group-limited sigmoid routing of section 10
+ * in place of the softmax (experts page, forward_sigmoid_grouped).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every pointer argument is a DEVICE pointer on the current HIP device,
@@ -184,14 +187,72 @@ int moe_forward(const void* x, int dt, const void* logits, int ldt,
                 size_t workspace_bytes, void* stream);
 
 /*
+ * moe_route_sigmoid_grouped - group-limited sigmoid routing (guide,
+ * section 10 "group-limited sigmoid MoE routing": route_sigmoid_grouped
+ * with GroupRoutingOptions).
+ *
+ *   logits  [T,E]      ldt      input
+ *   bias    [E]        float32  input, optional correction bias (NULL: none)
+ *   idx     [T,top_k]  uint32   output: chosen experts, best first
+ *   weights [T,top_k]  ldt      output: routing weights
+ *
+ * Per row: s_e is the FP32 sigmoid of logit e (evaluated in float64 and
+ * rounded once, so it is the correctly rounded value in all but ~1e-9 of
+ * cases) and c_e = s_e + bias[e] in FP32.  The experts form `groups` groups
+ * of E/groups consecutive ids.  A group's score is its largest c, or with
+ * group_top_two != 0 the FP32 sum of its two largest.  The selected_groups
+ * best groups are kept, then the top_k kept experts with the largest c are
+ * chosen and listed best first; ties, between groups and between experts,
+ * go to the smaller id.  The weight of a chosen expert is s_e (the bias only
+ * changes the choice), divided by the FP32 sum of the chosen s in slot
+ * order if renormalize != 0, then multiplied by scale and rounded (nearest
+ * even) to ldt.  A row whose c or group scores hold a NaN gets indices
+ * 0..top_k-1 and NaN weights; +inf and -inf logits are ordinary scores
+ * (1 and 0).  With renormalisation, a row whose chosen s are all 0 gets
+ * NaN weights (0/0).
+ * Limits of the guide, MOE_ERR_INVALID_ARG when violated: 1 <= E <= 1024;
+ * 1 <= groups <= 128 with E % groups == 0; 1 <= selected_groups <= groups;
+ * 1 <= top_k <= 64 and top_k <= selected_groups * E / groups;
+ * group_top_two needs E / groups >= 2; scale finite and > 0.
+ */
+int moe_route_sigmoid_grouped(const void* logits, int ldt, int64_t T,
+                              int64_t E, const float* bias, int64_t top_k,
+                              int64_t groups, int64_t selected_groups,
+                              int group_top_two, int renormalize, float scale,
+                              uint32_t* idx, void* weights, void* stream);
+
+/*
+ * moe_forward_sigmoid_grouped - the whole local MoE forward with
+ * group-limited sigmoid routing (experts page,
+ * SwiGluExperts::forward_sigmoid_grouped): moe_route_sigmoid_grouped ->
+ * moe_dispatch -> moe_experts_forward -> moe_combine on one stream.
+ *
+ * Arguments are those of moe_forward plus the routing options and the
+ * optional bias of moe_route_sigmoid_grouped; the workspace size is
+ * moe_forward_workspace_size(T, H, I, E, top_k, dt, ldt) (the same layout).
+ * Limits are those of moe_route_sigmoid_grouped and moe_forward.
+ */
+int moe_forward_sigmoid_grouped(const void* x, int dt, const void* logits,
+                                int ldt, const float* bias, int64_t T,
+                                int64_t H, int64_t I, int64_t E,
+                                int64_t top_k, int64_t groups,
+                                int64_t selected_groups, int group_top_two,
+                                int renormalize, float scale,
+                                const void* w_gate, const void* w_up,
+                                const void* w_down, void* out,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * moe_set_timing_events - instrumentation for measuring each kernel.
  *
  * events: `count` hipEvent_t handles created by the caller (hipEventCreate),
  * or NULL with count 0 to switch recording off.  While set, every
- * moe_forward call on this thread records events[0] on its stream before
- * its first kernel and events[i] right after its i-th kernel, so the
- * elapsed time between events[i-1] and events[i] is kernel i.  The kernels
- * of moe_forward, in order: 1 route, 2 dispatch count, 3 dispatch scan,
+ * moe_forward and moe_forward_sigmoid_grouped call on this thread records
+ * events[0] on its stream before its first kernel and events[i] right
+ * after its i-th kernel, so the elapsed time between events[i-1] and
+ * events[i] is kernel i.  The kernels of both forwards, in order: 1 route
+ * (softmax or group-limited sigmoid), 2 dispatch count, 3 dispatch scan,
  * 4 dispatch scatter, 5 gate+up GEMM with SwiGLU, 6 down GEMM, 7 combine.
  * count must be 0 or MOE_TIMING_EVENTS.  The library does not own the
  * events; the caller keeps them alive while recording is on.

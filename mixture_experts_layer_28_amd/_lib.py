@@ -19,6 +19,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 _SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
 SIGNATURES = {
     "moe_route": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _P, _P, _P]),
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I64, _I64]),
@@ -32,6 +33,13 @@ SIGNATURES = {
                                          _INT]),
     "moe_forward": (_INT, [_P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                            _INT, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_sigmoid_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _I64, _I64,
+                                         _I64, _INT, _INT, _F32, _P, _P,
+                                         _P]),
+    "moe_forward_sigmoid_grouped": (_INT, [_P, _INT, _P, _INT, _P, _I64, _I64,
+                                           _I64, _I64, _I64, _I64, _I64, _INT,
+                                           _INT, _F32, _P, _P, _P, _P, _P,
+                                           _SZ, _P]),
     "moe_set_timing_events": (_INT, [_P, _INT]),
     "moe_status_string": (ctypes.c_char_p, [_INT]),
     "moe_last_error": (ctypes.c_char_p, []),

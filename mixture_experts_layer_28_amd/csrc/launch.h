@@ -17,6 +17,22 @@ void timing_mark(int n, hipStream_t st);
 hipError_t launch_route(const void* logits, int ldt, int64_t T, int E, int k,
                         int renorm, uint32_t* idx, void* w, hipStream_t st);
 
+// Options of group-limited sigmoid routing, validated by the caller:
+// groups * gsz == E, 1 <= selected <= groups, gsz >= 2 if top_two.
+struct GroupRouting {
+  int groups;    // number of expert groups
+  int gsz;       // experts per group
+  int selected;  // groups kept per row
+  int top_two;   // group score: sum of the two largest (else the largest)
+  int renorm;    // renormalise the chosen weights
+  float scale;   // applied after renormalisation
+};
+// E <= 1024, k <= 64; bias may be null.
+hipError_t launch_route_sigmoid(const void* logits, int ldt, const float* bias,
+                                int64_t T, int E, int k,
+                                const GroupRouting& o, uint32_t* idx, void* w,
+                                hipStream_t st);
+
 // ---- dispatch --------------------------------------------------------------
 // Scratch layout: a table of per-chunk expert counts [nchunks][E+1] u32,
 // reused in place for the per-chunk row bases.

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -75,6 +76,44 @@ int check_route(const void* logits, int ldt, int64_t T, int64_t E,
   if (!bytes_ok(T, E, 4)) return fail(MOE_ERR_SHAPE, "moe_route: T*E overflows");
   if (T > 0 && (!logits || !idx || !w)) return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
   return MOE_OK;
+}
+
+// Limits of group-limited sigmoid routing (guide, section 10).
+constexpr int64_t kMaxSigmoidE = 1024;
+constexpr int64_t kMaxGroups = 128;
+constexpr int64_t kMaxSigmoidK = 64;
+
+int check_route_sigmoid(const void* logits, int ldt, int64_t T, int64_t E,
+                        int64_t k, int64_t groups, int64_t sel, int top_two,
+                        float scale, const void* idx, const void* w) {
+  const char* f = "moe_route_sigmoid_grouped";
+  if (!valid_dtype(ldt)) return fail(MOE_ERR_DTYPE, "%s: unknown logits dtype %d", f, ldt);
+  if (T < 0) return fail(MOE_ERR_SHAPE, "%s: T must be >= 0", f);
+  if (E < 1 || E > kMaxSigmoidE) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in 1..=%lld", f, (long long)kMaxSigmoidE);
+  if (groups < 1 || groups > kMaxGroups || E % groups != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: groups must be in 1..=%lld and divide E", f, (long long)kMaxGroups);
+  if (sel < 1 || sel > groups) return fail(MOE_ERR_INVALID_ARG, "%s: selected_groups must be in 1..=groups", f);
+  if (k < 1 || k > kMaxSigmoidK || k > sel * (E / groups))
+    return fail(MOE_ERR_INVALID_ARG, "%s: top_k must be in 1..=%lld and at most the experts of the selected groups", f, (long long)kMaxSigmoidK);
+  if (top_two && E / groups < 2) return fail(MOE_ERR_INVALID_ARG, "%s: group_top_two needs two experts per group", f);
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(MOE_ERR_INVALID_ARG, "%s: scale must be finite and positive", f);
+  int64_t n;
+  if (!mul_ok(T, k, &n) || n > kMaxRows) return fail(MOE_ERR_SHAPE, "%s: T*top_k must be < 2^32", f);
+  if (!bytes_ok(T, E, 4)) return fail(MOE_ERR_SHAPE, "%s: T*E overflows", f);
+  if (T > 0 && (!logits || !idx || !w)) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", f);
+  return MOE_OK;
+}
+
+moe::GroupRouting group_routing(int64_t E, int64_t groups, int64_t sel,
+                                int top_two, int renorm, float scale) {
+  moe::GroupRouting o;
+  o.groups = (int)groups;
+  o.gsz = (int)(E / groups);
+  o.selected = (int)sel;
+  o.top_two = top_two ? 1 : 0;
+  o.renorm = renorm ? 1 : 0;
+  o.scale = scale;
+  return o;
 }
 
 int check_dispatch(const void* x, int dt, int64_t T, int64_t H, int64_t E,
@@ -165,6 +204,72 @@ void timing_mark(int n, hipStream_t st) {
     (void)hipEventRecord(g_marks[n], st);
 }
 }  // namespace moe
+
+// The stages after routing, shared by both forwards: the checks that do
+// not depend on the routing method, the workspace carve-up and the launch
+// sequence.  `route(idx, w, stream)` launches the routing kernel.
+template <typename Route>
+int run_forward(const char* f, const void* x, int dt, int ldt, int64_t T,
+                int64_t H, int64_t I, int64_t E, int64_t top_k,
+                const void* w_gate, const void* w_up, const void* w_down,
+                void* out, void* workspace, size_t workspace_bytes,
+                void* stream, Route route) {
+  // x stands in for the workspace-resident offsets/act/y buffers here;
+  // the workspace itself is checked below.
+  int s = check_experts(x, dt, T * top_k, H, I, E, w_gate, w_up, w_down, x, x, x);
+  if (s != MOE_OK) return s;
+  if (T > 0 && (!x || !out)) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", f);
+  if (top_k > kMaxCombineK) return fail(MOE_ERR_UNSUPPORTED, "%s: top_k > %lld", f, (long long)kMaxCombineK);
+  const size_t need = moe_forward_workspace_size(T, H, I, E, top_k, dt, ldt);
+  if (need == 0) return fail(MOE_ERR_SHAPE, "%s: sizes out of range", f);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace needs %zu bytes", f, need);
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", f);
+  if (T == 0) return ok();
+
+  const ForwardLayout L = forward_layout(T, H, I, E, top_k, dt, ldt);
+  char* ws = (char*)workspace;
+  uint32_t* idx = (uint32_t*)(ws + L.idx);
+  void* w = ws + L.w;
+  uint32_t* offsets = (uint32_t*)(ws + L.offsets);
+  uint32_t* row_expert = (uint32_t*)(ws + L.row_expert);
+  uint32_t* row_token = (uint32_t*)(ws + L.row_token);
+  uint32_t* token_row = (uint32_t*)(ws + L.token_row);
+  void* xd = ws + L.xd;
+  void* dws = ws + L.dws;
+  void* act = ws + L.act;
+  void* y = ws + L.y;
+  const int64_t N = T * top_k;
+  const hipStream_t st = (hipStream_t)stream;
+  char what[96];
+
+  struct Marking {
+    Marking() { g_in_forward = true; }
+    ~Marking() { g_in_forward = false; }
+  } marking;
+  moe::timing_mark(0, st);
+  hipError_t err = route(idx, w, st);
+  std::snprintf(what, sizeof(what), "%s(route)", f);
+  if (err != hipSuccess) return hip_status(err, what);
+  moe::timing_mark(1, st);
+  err = moe::launch_dispatch(x, dt, T, H, (int)E, (int)top_k, idx, xd,
+                             offsets, row_expert, row_token, token_row, dws,
+                             moe::plan_dispatch(T, E, top_k), st);
+  std::snprintf(what, sizeof(what), "%s(dispatch)", f);
+  if (err != hipSuccess) return hip_status(err, what);
+  moe::timing_mark(4, st);
+  err = moe::launch_experts(xd, dt, N, H, I, (int)E, w_gate, w_up, w_down,
+                            offsets, act, y, st);
+  std::snprintf(what, sizeof(what), "%s(experts)", f);
+  if (err != hipSuccess) return hip_status(err, what);
+  moe::timing_mark(6, st);
+  err = moe::launch_combine(y, dt, N, T, H, (int)top_k, w, ldt, token_row,
+                            out, st);
+  moe::timing_mark(7, st);
+  std::snprintf(what, sizeof(what), "%s(combine)", f);
+  return hip_status(err, what);
+}
 
 extern "C" {
 
@@ -285,59 +390,58 @@ int moe_forward(const void* x, int dt, const void* logits, int ldt,
                 int renormalize, const void* w_gate, const void* w_up,
                 const void* w_down, void* out, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  int s = check_route(logits, ldt, T, E, top_k, workspace, workspace);
+  const int s = check_route(logits, ldt, T, E, top_k, workspace, workspace);
   if (s != MOE_OK) return s;
-  // x stands in for the workspace-resident offsets/act/y buffers here;
-  // the workspace itself is checked below.
-  s = check_experts(x, dt, T * top_k, H, I, E, w_gate, w_up, w_down, x, x, x);
+  return run_forward(
+      "moe_forward", x, dt, ldt, T, H, I, E, top_k, w_gate, w_up, w_down, out,
+      workspace, workspace_bytes, stream,
+      [&](uint32_t* idx, void* w, hipStream_t st) {
+        return moe::launch_route(logits, ldt, T, (int)E, (int)top_k,
+                                 renormalize ? 1 : 0, idx, w, st);
+      });
+}
+
+int moe_route_sigmoid_grouped(const void* logits, int ldt, int64_t T,
+                              int64_t E, const float* bias, int64_t top_k,
+                              int64_t groups, int64_t selected_groups,
+                              int group_top_two, int renormalize, float scale,
+                              uint32_t* idx, void* weights, void* stream) {
+  const int s = check_route_sigmoid(logits, ldt, T, E, top_k, groups,
+                                    selected_groups, group_top_two, scale,
+                                    idx, weights);
   if (s != MOE_OK) return s;
-  if (T > 0 && (!x || !out)) return fail(MOE_ERR_INVALID_ARG, "moe_forward: null pointer");
-  if (top_k > kMaxCombineK) return fail(MOE_ERR_UNSUPPORTED, "moe_forward: top_k > %lld", (long long)kMaxCombineK);
-  const size_t need = moe_forward_workspace_size(T, H, I, E, top_k, dt, ldt);
-  if (need == 0) return fail(MOE_ERR_SHAPE, "moe_forward: sizes out of range");
-  if (!workspace || workspace_bytes < need)
-    return fail(MOE_ERR_INVALID_ARG, "moe_forward: workspace needs %zu bytes", need);
-  if ((uintptr_t)workspace % 256 != 0)
-    return fail(MOE_ERR_INVALID_ARG, "moe_forward: workspace must be 256-byte aligned");
   if (T == 0) return ok();
+  const moe::GroupRouting o = group_routing(E, groups, selected_groups,
+                                            group_top_two, renormalize, scale);
+  return hip_status(moe::launch_route_sigmoid(logits, ldt, bias, T, (int)E,
+                                              (int)top_k, o, idx, weights,
+                                              (hipStream_t)stream),
+                    "moe_route_sigmoid_grouped");
+}
 
-  const ForwardLayout L = forward_layout(T, H, I, E, top_k, dt, ldt);
-  char* ws = (char*)workspace;
-  uint32_t* idx = (uint32_t*)(ws + L.idx);
-  void* w = ws + L.w;
-  uint32_t* offsets = (uint32_t*)(ws + L.offsets);
-  uint32_t* row_expert = (uint32_t*)(ws + L.row_expert);
-  uint32_t* row_token = (uint32_t*)(ws + L.row_token);
-  uint32_t* token_row = (uint32_t*)(ws + L.token_row);
-  void* xd = ws + L.xd;
-  void* dws = ws + L.dws;
-  void* act = ws + L.act;
-  void* y = ws + L.y;
-  const int64_t N = T * top_k;
-  const hipStream_t st = (hipStream_t)stream;
-
-  struct Marking {
-    Marking() { g_in_forward = true; }
-    ~Marking() { g_in_forward = false; }
-  } marking;
-  moe::timing_mark(0, st);
-  hipError_t err = moe::launch_route(logits, ldt, T, (int)E, (int)top_k,
-                                     renormalize ? 1 : 0, idx, w, st);
-  if (err != hipSuccess) return hip_status(err, "moe_forward(route)");
-  moe::timing_mark(1, st);
-  err = moe::launch_dispatch(x, dt, T, H, (int)E, (int)top_k, idx, xd,
-                             offsets, row_expert, row_token, token_row, dws,
-                             moe::plan_dispatch(T, E, top_k), st);
-  if (err != hipSuccess) return hip_status(err, "moe_forward(dispatch)");
-  moe::timing_mark(4, st);
-  err = moe::launch_experts(xd, dt, N, H, I, (int)E, w_gate, w_up, w_down,
-                            offsets, act, y, st);
-  if (err != hipSuccess) return hip_status(err, "moe_forward(experts)");
-  moe::timing_mark(6, st);
-  err = moe::launch_combine(y, dt, N, T, H, (int)top_k, w, ldt, token_row,
-                            out, st);
-  moe::timing_mark(7, st);
-  return hip_status(err, "moe_forward(combine)");
+int moe_forward_sigmoid_grouped(const void* x, int dt, const void* logits,
+                                int ldt, const float* bias, int64_t T,
+                                int64_t H, int64_t I, int64_t E,
+                                int64_t top_k, int64_t groups,
+                                int64_t selected_groups, int group_top_two,
+                                int renormalize, float scale,
+                                const void* w_gate, const void* w_up,
+                                const void* w_down, void* out,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  const int s = check_route_sigmoid(logits, ldt, T, E, top_k, groups,
+                                    selected_groups, group_top_two, scale,
+                                    workspace, workspace);
+  if (s != MOE_OK) return s;
+  const moe::GroupRouting o = group_routing(E, groups, selected_groups,
+                                            group_top_two, renormalize, scale);
+  return run_forward(
+      "moe_forward_sigmoid_grouped", x, dt, ldt, T, H, I, E, top_k, w_gate,
+      w_up, w_down, out, workspace, workspace_bytes, stream,
+      [&](uint32_t* idx, void* w, hipStream_t st) {
+        return moe::launch_route_sigmoid(logits, ldt, bias, T, (int)E,
+                                         (int)top_k, o, idx, w, st);
+      });
 }
 
 }  // extern "C"

@@ -193,6 +193,64 @@ def moe_forward(x, logits, w_gate, w_up, w_down, top_k, renormalize=True,
     return out
 
 
+def _bias(bias, E, dev):
+    """The optional FP32 correction bias [E] (None: no correction)."""
+    if bias is None:
+        return None
+    bias = _c(bias)
+    if (bias.dtype != torch.float32 or tuple(bias.shape) != (E,)
+            or bias.device != dev):
+        raise ValueError("bias must be a float32 tensor of shape (%d,) on %s"
+                         % (E, dev))
+    return bias
+
+
+def moe_route_sigmoid_grouped(logits, top_k, groups, selected_groups,
+                              bias=None, group_top_two=False,
+                              renormalize=True, scale=1.0, idx=None,
+                              weights=None):
+    """Group-limited sigmoid routing.  logits [T,E], bias None or float32
+    [E] -> (idx int32 [T,k], weights [T,k] in the logits dtype)."""
+    logits = _c(logits)
+    dev = _dev(logits)
+    T, E = logits.shape
+    bias = _bias(bias, E, dev)
+    idx = _out(idx, (T, top_k), _U32, dev, "idx")
+    weights = _out(weights, (T, top_k), logits.dtype, dev, "weights")
+    check(lib().moe_route_sigmoid_grouped(
+        _p(logits), _dt(logits, "logits"), T, E, _p(bias), top_k, groups,
+        selected_groups, int(bool(group_top_two)), int(bool(renormalize)),
+        float(scale), _p(idx), _p(weights), _stream(dev)))
+    return idx, weights
+
+
+def moe_forward_sigmoid_grouped(x, logits, w_gate, w_up, w_down, top_k,
+                                groups, selected_groups, bias=None,
+                                group_top_two=False, renormalize=True,
+                                scale=1.0, out=None, workspace=None):
+    """Whole forward with group-limited sigmoid routing, one call."""
+    x, logits = _c(x), _c(logits)
+    w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
+    dev = _dev(x, logits, w_gate, w_up, w_down)
+    T, H = x.shape
+    E, I = _experts_weights(w_gate, w_up, w_down, H, x.dtype)
+    if logits.shape != (T, E):
+        raise ValueError("logits must be [T, E]")
+    bias = _bias(bias, E, dev)
+    workspace, ws_bytes = _workspace(
+        workspace,
+        moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype),
+        dev)
+    out = _out(out, (T, H), x.dtype, dev, "out")
+    check(lib().moe_forward_sigmoid_grouped(
+        _p(x), _dt(x, "x"), _p(logits), _dt(logits, "logits"), _p(bias), T,
+        H, I, E, top_k, groups, selected_groups, int(bool(group_top_two)),
+        int(bool(renormalize)), float(scale), _p(w_gate), _p(w_up),
+        _p(w_down), _p(out), _p(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
 __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_experts_forward", "moe_combine", "moe_forward",
-           "moe_forward_workspace_size", "_lib"]
+           "moe_forward_workspace_size", "moe_route_sigmoid_grouped",
+           "moe_forward_sigmoid_grouped", "_lib"]

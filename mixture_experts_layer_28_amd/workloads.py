@@ -15,12 +15,16 @@ Workloads (sizes: T tokens, H hidden, I intermediate, E experts, k top-k):
              per-expert logit bias (std 2) skews the load so that some
              experts receive no token
 * ``decode`` bf16, T=32 or 256, H=4096, I=1536, E=128, k=8, not renormalised
+* ``grouped`` bf16, the ``fine`` layer shape (T=8192, H=7168, I=2048, E=64,
+             k=8) under group-limited sigmoid routing: 8 groups of 8
+             experts, 4 groups kept, group score = sum of the two largest,
+             renormalised, scale 2.5, FP32 correction bias N(0, 0.25)
 
 Distributions: "N(0, s)" means standard deviation s.  Inputs and logits are
 N(0,1).  ``tiny`` and ``edge`` draw gate/up with std 1/sqrt(H) and down with
 std 1/sqrt(I); the bf16 workloads use std 0.02 for every expert weight.
 
-Random streams: workload number c (tiny=1 ... decode=5) seeds
+Random streams: workload number c (tiny=1 ... grouped=6) seeds
 ``numpy.random.SeedSequence(1000 + c)`` and spawns one child per tensor
 (x, logits, gate, up, down, bias, edge rows).  x, logits, bias and the edge
 rows come from numpy PCG64 in float32 and are rounded to the storage dtype
@@ -48,6 +52,9 @@ WORKLOADS = {
                  renorm=True, w_std=0.02, bias_std=2.0),
     "decode": dict(num=5, fmt="bf16", T=32, H=4096, I=1536, E=128, k=8,
                    renorm=False, w_std=0.02, Ts=(32, 256)),
+    "grouped": dict(num=6, fmt="bf16", T=8192, H=7168, I=2048, E=64, k=8,
+                    renorm=True, w_std=0.02, groups=8, selected_groups=4,
+                    group_top_two=True, scale=2.5, corr_bias_std=0.25),
 }
 
 EDGE_ROWS = 25          # floor(0.05 * 512) rows of each poisoned kind
@@ -86,8 +93,9 @@ def make(name, device="cpu", T=None, k=None, renorm=None, H=None, I=None,
     them for ragged and edge shapes); the default is the named workload.
 
     Returns a dict: x [T,H], logits [T,E], w_gate/w_up [E,I,H],
-    w_down [E,H,I] (torch tensors on ``device``), plus k, renorm, fmt and the
-    sizes.
+    w_down [E,H,I] (torch tensors on ``device``), bias (the float32
+    correction bias [E] of group-limited routing, else None), plus k,
+    renorm, fmt, the sizes and, for ``grouped``, the routing options.
     """
     cfg = dict(WORKLOADS[name])
     T = cfg["T"] if T is None else T
@@ -118,6 +126,11 @@ def make(name, device="cpu", T=None, k=None, renorm=None, H=None, I=None,
         b = _normal(st["bias"], (E,)) * np.float32(cfg["bias_std"])
         z = (z + b[None, :]).astype(np.float32)
     logits = torch.from_numpy(z).to(tdt).to(device)
+    corr_bias = None
+    if "corr_bias_std" in cfg:
+        corr_bias = torch.from_numpy(
+            _normal(st["bias"], (E,)) * np.float32(cfg["corr_bias_std"])
+        ).to(device)
 
     if cfg["w_std"] == "fan_in":
         sg, sd = 1.0 / np.sqrt(H), 1.0 / np.sqrt(I)
@@ -126,8 +139,13 @@ def make(name, device="cpu", T=None, k=None, renorm=None, H=None, I=None,
     w_gate = _weights(st["gate"], E, I, H, sg, fmt, device)
     w_up = _weights(st["up"], E, I, H, sg, fmt, device)
     w_down = _weights(st["down"], E, H, I, sd, fmt, device)
-    return dict(x=x, logits=logits, w_gate=w_gate, w_up=w_up, w_down=w_down,
-                k=k, renorm=renorm, fmt=fmt, T=T, H=H, I=I, E=E, name=name)
+    out = dict(x=x, logits=logits, w_gate=w_gate, w_up=w_up, w_down=w_down,
+               k=k, renorm=renorm, fmt=fmt, T=T, H=H, I=I, E=E, name=name,
+               bias=corr_bias)
+    for key in ("groups", "selected_groups", "group_top_two", "scale"):
+        if key in cfg:
+            out[key] = cfg[key]
+    return out
 
 
 def to_numpy(t, fmt):

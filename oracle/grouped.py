@@ -40,6 +40,8 @@ the repository's design notes):
 * R-SCast   weights are computed in FP32 (renormalising denominator: the
             FP32 sum of the selected sigmoid values in slot order), then
             multiplied by the FP32 scale, then rounded to the logits dtype.
+            When every chosen sigmoid value is 0 the renormalised weights
+            are 0/0 = NaN, the plain result of the definition.
 """
 
 import math
@@ -47,7 +49,7 @@ import math
 import numpy as np
 
 from .fp import decode, round_to
-from .moe import combine, dispatch, experts
+from .moe import combine, dispatch, expert_rows, experts
 
 
 def check_options(E, k, groups, selected_groups, group_top_two, scale):
@@ -122,7 +124,8 @@ def route_sigmoid_grouped(logits, bias, k, groups, selected_groups,
             den = np.float32(0.0)
             for v in ws:
                 den = np.float32(den + v)
-            ws = (ws / den).astype(np.float32)
+            with np.errstate(invalid="ignore"):      # 0/0 stays NaN
+                ws = (ws / den).astype(np.float32)
         ws = (ws * sc).astype(np.float32)
         idx[t] = sel
         w[t] = round_to(ws.astype(np.float64), fmt)
@@ -142,3 +145,28 @@ def forward_sigmoid_grouped(x, logits, bias, w_gate, w_up, w_down, k, groups,
     y = experts(d["xd"], d["offsets"], w_gate, w_up, w_down, fmt)
     out = combine(y, w, d["token_row"], fmt)
     return {"idx": idx, "w": w, "dispatch": d, "y": y, "out": out}
+
+
+def forward_sigmoid_tokens(x, logits, bias, w_gate, w_up, w_down, k, groups,
+                           selected_groups, group_top_two, renormalize,
+                           scale, fmt, tokens, logits_fmt=None):
+    """The forward output for selected tokens only, computed token by token
+    (route the token's logits, apply its k experts to its row, combine), for
+    sizes where the full forward is too slow for the oracle."""
+    lfmt = fmt if logits_fmt is None else logits_fmt
+    x64 = decode(x, fmt)
+    idx, w = route_sigmoid_grouped(np.asarray(logits)[list(tokens)], bias, k,
+                                   groups, selected_groups, group_top_two,
+                                   renormalize, scale, lfmt)
+    out = np.zeros((len(tokens), x64.shape[1]), dtype=np.float64)
+    for n, t in enumerate(tokens):
+        acc = np.zeros(x64.shape[1], dtype=np.float64)
+        for j in range(k):
+            e = int(idx[n, j])
+            y = expert_rows(x64[t][None, :], e,
+                            decode(np.asarray(w_gate)[e], fmt),
+                            decode(np.asarray(w_up)[e], fmt),
+                            decode(np.asarray(w_down)[e], fmt), fmt)[0]
+            acc = acc + w[n, j] * y
+        out[n] = round_to(acc, fmt)
+    return idx, w, out

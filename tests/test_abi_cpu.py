@@ -148,3 +148,83 @@ def test_timing_events_rejects_wrong_counts():
     nulls = (ctypes.c_void_p * 8)()
     assert L.moe_set_timing_events(nulls, 8) == 1     # a null handle
     assert L.moe_set_timing_events(None, 0) == 0      # switching off is fine
+
+
+# moe_route_sigmoid_grouped(logits, ldt, T, E, bias, top_k, groups,
+#                           selected_groups, group_top_two, renormalize,
+#                           scale, idx, weights, stream)
+_SIG = [FAKE, 2, 16, 64, None, 8, 8, 4, 1, 1, 2.5, FAKE, FAKE, None]
+
+
+@pytest.mark.parametrize("i,v,status", [
+    (1, 9, 3),            # bad dtype
+    (2, -1, 2),           # T < 0
+    (3, 0, 1),            # E = 0
+    (3, 1025, 1),         # E beyond 1..=1024
+    (6, 0, 1),            # groups = 0
+    (6, 7, 1),            # groups does not divide E
+    (7, 0, 1),            # selected_groups = 0
+    (7, 9, 1),            # selected_groups > groups
+    (5, 0, 1),            # top_k = 0
+    (5, 65, 1),           # top_k > 64
+    (10, 0.0, 1),         # scale not positive
+    (10, -2.0, 1),
+    (10, float("inf"), 1),
+    (10, float("nan"), 1),
+    (0, None, 1),         # null logits
+    (11, None, 1),        # null idx
+    (2, 1 << 30, 2),      # T*top_k >= 2^32
+])
+def test_route_sigmoid_rejects(i, v, status):
+    a = list(_SIG)
+    a[i] = v
+    assert _lib.lib().moe_route_sigmoid_grouped(*a) == status, (i, v)
+    assert _last()
+
+
+def test_route_sigmoid_group_limits():
+    L = _lib.lib()
+    a = list(_SIG)
+    a[5], a[7] = 33, 4   # 4 groups of 8 experts hold only 32
+    assert L.moe_route_sigmoid_grouped(*a) == 1 and "top_k" in _last()
+    a = list(_SIG)
+    a[3], a[6] = 128, 128  # groups of one expert cannot sum a top two
+    a[7] = 8
+    assert L.moe_route_sigmoid_grouped(*a) == 1 and "two" in _last()
+    a = list(_SIG)
+    a[3], a[6], a[7], a[5] = 512, 256, 8, 8   # more than 128 groups
+    assert L.moe_route_sigmoid_grouped(*a) == 1
+    a = list(_SIG)
+    a[3], a[6], a[5] = 1024, 16, 65           # top_k > 64 though 4*64 fit
+    assert L.moe_route_sigmoid_grouped(*a) == 1 and "top_k" in _last()
+    # T = 0 with every option valid: nothing to do
+    a = list(_SIG)
+    a[2], a[0], a[11], a[12] = 0, None, None, None
+    assert L.moe_route_sigmoid_grouped(*a) == 0 and _last() == ""
+    a[3], a[6], a[7], a[5], a[8] = 1024, 128, 128, 64, 1  # the largest case
+    assert L.moe_route_sigmoid_grouped(*a) == 0
+
+
+def test_forward_sigmoid_rejects():
+    L = _lib.lib()
+    ws = L.moe_forward_workspace_size(64, 128, 256, 64, 8, 2, 2)
+    args = [FAKE, 2, FAKE, 2, None, 64, 128, 256, 64, 8, 8, 4, 1, 1, 2.5,
+            FAKE, FAKE, FAKE, FAKE, 0x10000, ws, None]
+    a = list(args)
+    a[20] = ws - 1
+    assert L.moe_forward_sigmoid_grouped(*a) == 1 and "workspace" in _last()
+    a = list(args)
+    a[19] = 0x10010  # not 256-byte aligned
+    assert L.moe_forward_sigmoid_grouped(*a) == 1
+    a = list(args)
+    a[10] = 5        # groups does not divide E
+    assert L.moe_forward_sigmoid_grouped(*a) == 1 and "groups" in _last()
+    a = list(args)
+    a[15] = None     # a weight pointer
+    assert L.moe_forward_sigmoid_grouped(*a) == 1
+    a = list(args)
+    a[14] = 0.0      # scale
+    assert L.moe_forward_sigmoid_grouped(*a) == 1 and "scale" in _last()
+    a = list(args)
+    a[5] = 0         # T = 0: nothing to do
+    assert L.moe_forward_sigmoid_grouped(*a) == 0

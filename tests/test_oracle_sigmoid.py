@@ -16,7 +16,8 @@ Pins, none of which reuses the oracle's own formulation:
   bias; renormalised weights sum to ``scale``;
 * the option limits of the section;
 * the forward equals a per-token sum over the chosen experts, and with
-  identical experts the expert output times the summed weights.
+  identical experts the expert output times the summed weights; the
+  token-by-token form agrees with the full forward.
 """
 
 import itertools
@@ -30,7 +31,8 @@ from scipy.special import expit
 
 from oracle.fp import round_to
 from oracle.grouped import (check_options, forward_sigmoid_grouped,
-                            route_sigmoid_grouped, sigmoid_fp32)
+                            forward_sigmoid_tokens, route_sigmoid_grouped,
+                            sigmoid_fp32)
 from oracle.moe import expert_rows
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden",
@@ -307,3 +309,18 @@ def test_forward_with_identical_experts():
                     wu[0].astype(np.float64), wd[0].astype(np.float64), "f32")
     want = round_to(r["w"].sum(axis=1)[:, None] * y, "f32")
     assert np.allclose(r["out"], want, rtol=1e-6, atol=1e-7)
+
+
+def test_token_by_token_forward_matches_full_forward():
+    rng = np.random.default_rng(23)
+    T, H, I, E = 7, 8, 12, 16
+    x, lg, wg, wu, wd = _small_layer(rng, T, H, I, E)
+    bias = (rng.standard_normal(E) * 0.2).astype(np.float32)
+    full = forward_sigmoid_grouped(x, lg, bias, wg, wu, wd, 4, 4, 2, True,
+                                   True, 2.5, "f32")
+    tokens = [0, 3, 6]
+    idx, w, out = forward_sigmoid_tokens(x, lg, bias, wg, wu, wd, 4, 4, 2,
+                                         True, True, 2.5, "f32", tokens)
+    assert np.array_equal(idx, full["idx"][tokens])
+    assert np.array_equal(w, full["w"][tokens])
+    assert np.allclose(out, full["out"][tokens], rtol=1e-6, atol=1e-7)
