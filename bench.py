@@ -62,10 +62,11 @@ def parse():
                         "calibration), update profiles/traffic.json and print "
                         "a markdown table")
     p.add_argument("--route-sweep", action="store_true",
-                   help="extension, not the benchmark: time moe_route alone "
-                        "at T = 2^16, 2^18, 2^20 (bf16 logits, E and k as "
-                        "listed in ROUTE_SWEEP) with the Infinity Cache "
-                        "flushed before each call; one JSON line per case")
+                   help="extension, not the benchmark: time moe_route and "
+                        "moe_route_sigmoid_grouped alone at T = 2^16, 2^18, "
+                        "2^20 (bf16 logits, the cases listed in ROUTE_SWEEP) "
+                        "with the Infinity Cache flushed before each call; "
+                        "one JSON line per case")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU work: print the kernel statistics of a "
                         "rocprofv3 --kernel-trace --stats run as markdown")
@@ -208,25 +209,40 @@ def record_traffic(workload, prof_dir, copy_dir):
     print("\n".join(lines))
 
 
-ROUTE_SWEEP = [(8, 2), (64, 8), (128, 8), (256, 8)]  # (E, top_k)
+# (router, E, top_k, groups, selected_groups); the sigmoid cases keep the top
+# two of each group's scores
+ROUTE_SWEEP = [("softmax", 8, 2, 0, 0), ("softmax", 64, 8, 0, 0),
+               ("softmax", 128, 8, 0, 0), ("softmax", 256, 8, 0, 0),
+               ("sigmoid", 64, 8, 8, 4), ("sigmoid", 256, 8, 8, 4)]
 
 
 def route_sweep():
-    """Streaming efficiency of the route kernel on its own at large T (the
-    benchmark workloads hold at most 1.5 MB of logits, far below where HBM
-    bandwidth decides).  Bytes: T*E logits read + T*k*(4 + 2) written."""
+    """Streaming efficiency of the routing kernels on their own at large T
+    (the benchmark workloads hold at most 1.5 MB of logits, far below where
+    HBM bandwidth decides).  Bytes: T*E logits read + T*k*(4 + 2) written
+    (+ 4*E of bias for the sigmoid router)."""
     import statistics
     import torch
     import mixture_experts_layer_28_amd as moe
     flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
     gen = torch.Generator(device="cuda").manual_seed(7)
-    for E, k in ROUTE_SWEEP:
+    for kind, E, k, groups, sel in ROUTE_SWEEP:
+        bias = torch.randn(E, device="cuda", generator=gen) * 0.25
         for T in (1 << 16, 1 << 18, 1 << 20):
             lg = torch.randn(T, E, device="cuda", generator=gen).to(
                 torch.bfloat16)
             idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
             w = torch.empty(T, k, dtype=torch.bfloat16, device="cuda")
-            moe.moe_route(lg, k, True, idx, w)
+
+            def call():
+                if kind == "softmax":
+                    moe.moe_route(lg, k, True, idx, w)
+                else:
+                    moe.moe_route_sigmoid_grouped(
+                        lg, k, groups, sel, bias=bias, group_top_two=True,
+                        renormalize=True, scale=2.5, idx=idx, weights=w)
+
+            call()
             torch.cuda.synchronize()
             ts = []
             for _ in range(7):
@@ -234,14 +250,17 @@ def route_sweep():
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record()
-                moe.moe_route(lg, k, True, idx, w)
+                call()
                 b.record()
                 torch.cuda.synchronize()
                 ts.append(a.elapsed_time(b))
             ms = statistics.median(ts)
-            nbytes = T * E * 2 + T * k * 6
-            print(json.dumps({"extension": "route_sweep", "E": E, "top_k": k,
-                              "T": T, "us": round(ms * 1e3, 1),
+            nbytes = T * E * 2 + T * k * 6 + (E * 4 if kind != "softmax"
+                                              else 0)
+            print(json.dumps({"extension": "route_sweep", "router": kind,
+                              "E": E, "top_k": k, "groups": groups,
+                              "selected_groups": sel, "T": T,
+                              "us": round(ms * 1e3, 1),
                               "GB/s": round(nbytes / ms / 1e6, 1),
                               "hbm_frac": round(nbytes / ms / 1e6 /
                                                 PEAK_HBM_GBS, 4)}),

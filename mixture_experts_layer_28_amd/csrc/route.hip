@@ -31,16 +31,15 @@ namespace moe {
 namespace {
 
 // Register-cached path: E <= G * PL <= 1024.  VEC: every lane's PL values
-// are one or more aligned 16-byte vectors of the row.
+// are one or more aligned 16-byte vectors of the row.  One row (< T) per
+// group of G lanes; returning ends this row only.
 template <int LDT, int G, int PL, bool VEC>
-__global__ __launch_bounds__(256) void route_kernel(
-    const typename Storage<LDT>::T* __restrict__ logits, int64_t T, int E,
+__device__ __forceinline__ void route_row(
+    const typename Storage<LDT>::T* __restrict__ logits, int64_t row, int E,
     int k, int renorm, uint32_t* __restrict__ idx,
     typename Storage<LDT>::T* __restrict__ w) {
   using S = typename Storage<LDT>::T;
   const int lane = threadIdx.x % G;
-  const int64_t row = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
-  if (row >= T) return;  // uniform across the group
   const S* src = logits + row * (int64_t)E + lane * PL;
   const int e0 = lane * PL;
 
@@ -139,18 +138,32 @@ __global__ __launch_bounds__(256) void route_kernel(
   }
 }
 
+// Rows are walked in a grid-stride loop over a grid of at most kMaxBlocks
+// workgroups, so a launch stays within the 2^32 work-item limit whatever T
+// is (a group's rows are uniform across its lanes).
+constexpr int64_t kMaxBlocks = 65536;
+
+template <int LDT, int G, int PL, bool VEC>
+__global__ __launch_bounds__(256) void route_kernel(
+    const typename Storage<LDT>::T* __restrict__ logits, int64_t T, int E,
+    int k, int renorm, uint32_t* __restrict__ idx,
+    typename Storage<LDT>::T* __restrict__ w) {
+  constexpr int R = 256 / G;
+  for (int64_t row = (int64_t)blockIdx.x * R + threadIdx.x / G; row < T;
+       row += (int64_t)gridDim.x * R)
+    route_row<LDT, G, PL, VEC>(logits, row, E, k, renorm, idx, w);
+}
+
 // Wide rows (E > 1024): one wave per row, values re-read each round; with
 // renormalisation a first pass over the k rounds computes the denominator.
 template <int LDT>
-__global__ __launch_bounds__(256) void route_wide_kernel(
-    const typename Storage<LDT>::T* __restrict__ logits, int64_t T, int E,
+__device__ __forceinline__ void route_wide_row(
+    const typename Storage<LDT>::T* __restrict__ logits, int64_t row, int E,
     int k, int renorm, uint32_t* __restrict__ idx,
     typename Storage<LDT>::T* __restrict__ w) {
   using S = typename Storage<LDT>::T;
   constexpr int G = 64;
   const int lane = threadIdx.x % G;
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / G;
-  if (row >= T) return;
   const S* src = logits + row * (int64_t)E;
   uint32_t* idx_row = idx + row * (int64_t)k;
   S* w_row = w + row * (int64_t)k;
@@ -201,12 +214,23 @@ __global__ __launch_bounds__(256) void route_wide_kernel(
   }
 }
 
+template <int LDT>
+__global__ __launch_bounds__(256) void route_wide_kernel(
+    const typename Storage<LDT>::T* __restrict__ logits, int64_t T, int E,
+    int k, int renorm, uint32_t* __restrict__ idx,
+    typename Storage<LDT>::T* __restrict__ w) {
+  for (int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64; row < T;
+       row += (int64_t)gridDim.x * 4)
+    route_wide_row<LDT>(logits, row, E, k, renorm, idx, w);
+}
+
 template <int LDT, int G, int PL>
 hipError_t launch_g(const void* logits, int64_t T, int E, int k, int renorm,
                     uint32_t* idx, void* w, hipStream_t st) {
   using S = typename Storage<LDT>::T;
   const int rows = 256 / G;
-  const dim3 grid((unsigned)((T + rows - 1) / rows));
+  const int64_t blocks = (T + rows - 1) / rows;
+  const dim3 grid((unsigned)(blocks < kMaxBlocks ? blocks : kMaxBlocks));
   // 16-byte loads when every lane's PL values are whole aligned vectors
   const bool vec = (PL * sizeof(S)) % 16 == 0 && E == G * PL &&
                    (uintptr_t)logits % 16 == 0;
@@ -231,7 +255,8 @@ hipError_t launch_route_t(const void* logits, int64_t T, int E, int k,
   if (E <= 256) return launch_g<LDT, 32, 8>(logits, T, E, k, renorm, idx, w, st);
   if (E <= 512) return launch_g<LDT, 64, 8>(logits, T, E, k, renorm, idx, w, st);
   if (E <= 1024) return launch_g<LDT, 64, 16>(logits, T, E, k, renorm, idx, w, st);
-  const dim3 grid((unsigned)((T + 3) / 4));
+  const int64_t blocks = (T + 3) / 4;
+  const dim3 grid((unsigned)(blocks < kMaxBlocks ? blocks : kMaxBlocks));
   hipLaunchKernelGGL((route_wide_kernel<LDT>), grid, dim3(256), 0, st,
                      (const S*)logits, T, E, k, renorm, idx, (S*)w);
   return hipGetLastError();

@@ -124,3 +124,23 @@ def test_largest_expert_count(k):
     for fmt in ("f32", "bf16"):
         _check(torch.from_numpy(lg).to(TDT[fmt]), k, True,
                "E=65536 k=%d %s" % (k, fmt))
+
+
+@pytest.mark.parametrize("E", [1024, 1500])
+def test_many_rows_wrap_the_grid(E):
+    """More rows than one pass of the capped grid covers (65536 blocks of 4
+    rows for E = 1024 and for the wide-row kernel): rows on both sides of
+    the wrap, sampled."""
+    k = 8
+    T = 65536 * 4 + 37
+    gen = torch.Generator(device="cuda").manual_seed(E)
+    lg = torch.randn((T, E), generator=gen, device="cuda").to(torch.bfloat16)
+    print("case: T=%d E=%d" % (T, E), flush=True)
+    idx_g, w_g = moe.moe_route(lg, k, True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 262143, 262144, 262145, T - 1] + list(
+        np.random.default_rng(0).choice(T, size=10, replace=False))
+    sel = torch.tensor(rows, device="cuda")
+    idx_r, w_r = route(values(lg[sel]), k, True, "bf16")
+    np.testing.assert_array_equal(u32(idx_g[sel]), idx_r)
+    assert_close(values(w_g[sel]), w_r, "bf16", "wrap E=%d" % E)
