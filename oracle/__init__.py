@@ -30,8 +30,14 @@ Parity status of each function (what pins it is listed in the test files
 * ``grouped.forward_sigmoid_grouped`` pinned (per-token sum, identical
                               experts)
 
+* ``router_weights.selected_router_weights`` / ``selected_router_backward``
+                              pinned (torch autograd in float64, finite
+                              differences, closed forms, invariants)
+
 ``grouped`` follows section 10 of the same guide (group-limited sigmoid
-routing) and the experts page's ``forward_sigmoid_grouped``.
+routing) and the experts page's ``forward_sigmoid_grouped``;
+``router_weights`` follows section 12 (router weights of a fixed selection
+and their logits gradient).
 """
 
-from . import fp, grouped, moe  # noqa: F401
+from . import fp, grouped, moe, router_weights  # noqa: F401
