@@ -67,6 +67,11 @@ def parse():
                         "2^20 (bf16 logits, the cases listed in ROUTE_SWEEP) "
                         "with the Infinity Cache flushed before each call; "
                         "one JSON line per case")
+    p.add_argument("--router-weights-sweep", action="store_true",
+                   help="extension, not the benchmark: time "
+                        "moe_selected_router_weights and "
+                        "moe_selected_router_backward alone at T = 2^16, "
+                        "2^18, 2^20; one JSON line per case")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU work: print the kernel statistics of a "
                         "rocprofv3 --kernel-trace --stats run as markdown")
@@ -267,6 +272,59 @@ def route_sweep():
                   flush=True)
 
 
+ROUTER_WEIGHTS_SWEEP = [(64, 8), (256, 8)]  # (E, top_k), int64 indices
+
+
+def router_weights_sweep():
+    """The router-weight kernels of a fixed selection (weights, then the
+    logits gradient) on their own at large T, bf16 logits, softmax scoring,
+    renormalised, Infinity Cache flushed before each call.  Algorithmic
+    bytes: weights T*E*2 logits + T*k*8 indices read, T*k*4 written;
+    backward the same reads plus T*k*4 grad_weights, T*E*2 written."""
+    import statistics
+    import torch
+    import mixture_experts_layer_28_amd as moe
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    for E, k in ROUTER_WEIGHTS_SWEEP:
+        for T in (1 << 16, 1 << 18, 1 << 20):
+            lg = torch.randn(T, E, device="cuda", generator=gen).to(
+                torch.bfloat16)
+            ind = torch.topk(lg.float(), k, dim=1).indices.contiguous()
+            g = torch.randn(T, k, device="cuda", generator=gen)
+            w = torch.empty(T, k, device="cuda")
+            dx = torch.empty(T, E, device="cuda", dtype=torch.bfloat16)
+            calls = {
+                "weights": (lambda: moe.moe_selected_router_weights(
+                    lg, ind, "softmax", True, 1.0, out=w),
+                    T * E * 2 + T * k * 8 + T * k * 4),
+                "backward": (lambda: moe.moe_selected_router_backward(
+                    lg, ind, g, "softmax", True, 1.0, out=dx),
+                    T * E * 2 + T * k * 12 + T * E * 2),
+            }
+            for name, (call, nbytes) in calls.items():
+                call()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(7):
+                    flush.fill_(1)
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    call()
+                    b.record()
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                ms = statistics.median(ts)
+                print(json.dumps({"extension": "router_weights_sweep",
+                                  "kernel": name, "E": E, "top_k": k,
+                                  "T": T, "us": round(ms * 1e3, 1),
+                                  "GB/s": round(nbytes / ms / 1e6, 1),
+                                  "hbm_frac": round(nbytes / ms / 1e6 /
+                                                    PEAK_HBM_GBS, 4)}),
+                      flush=True)
+
+
 def summarize_trace(trace_dir):
     """Markdown table of a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -357,6 +415,9 @@ def main():
         return
     if args.route_sweep:
         route_sweep()
+        return
+    if args.router_weights_sweep:
+        router_weights_sweep()
         return
     if args.copy_calibration:
         copy_calibration()

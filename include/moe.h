@@ -53,6 +53,17 @@ typedef enum moe_dtype {
     MOE_BF16 = 2
 } moe_dtype;
 
+typedef enum moe_index_type {
+    MOE_IDX_U32 = 0,
+    MOE_IDX_I32 = 1,
+    MOE_IDX_I64 = 2
+} moe_index_type;
+
+typedef enum moe_scoring {
+    MOE_SCORE_SOFTMAX = 0,
+    MOE_SCORE_SIGMOID = 1
+} moe_scoring;
+
 typedef enum moe_status {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1, /* null pointer, top_k out of range, ...   */
@@ -242,6 +253,64 @@ int moe_forward_sigmoid_grouped(const void* x, int dt, const void* logits,
                                 const void* w_down, void* out,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * moe_selected_router_weights - FP32 router weights of a fixed selection
+ * (guide, section 12 "first-order MoE training": selected_router_weights
+ * with RouterWeightOptions).
+ *
+ *   logits  [T,E]      ldt         input
+ *   indices [T,top_k]  index_type  input: experts of each row (moe_index_type)
+ *   weights [T,top_k]  float32     output
+ *
+ * Scores: scoring MOE_SCORE_SOFTMAX takes the softmax over all E experts of
+ * the row, MOE_SCORE_SIGMOID the sigmoid of each logit (FP32).  Slot j's
+ * weight is the score of expert indices[t,j] (a repeated index gathers the
+ * same score again); with renormalize != 0 divided by the sum of the row's
+ * selected scores; then multiplied by scale.  An invalid index (negative,
+ * or >= E) makes the whole row NaN, without an out-of-bounds access; NaN
+ * also follows from the scores (softmax: a row holding a NaN, a +inf or
+ * only -inf; sigmoid: a NaN logit, or a zero sum when renormalising).
+ * Limits, MOE_ERR_INVALID_ARG when violated: 1 <= top_k <= min(E, 64),
+ * E < 2^31, scale finite and > 0, scoring and index_type known.
+ */
+int moe_selected_router_weights(const void* logits, int ldt, int64_t T,
+                                int64_t E, const void* indices,
+                                int index_type, int64_t top_k, int scoring,
+                                int renormalize, float scale, float* weights,
+                                void* stream);
+
+/*
+ * moe_selected_router_backward - the logits gradient of
+ * moe_selected_router_weights (guide, section 12: selected_router_backward).
+ *
+ *   logits       [T,E]      ldt         input (the same as for the weights)
+ *   indices      [T,top_k]  index_type  input
+ *   grad_weights [T,top_k]  float32     input: dL/dweights
+ *   grad_logits  [T,E]      ldt         output: dL/dlogits
+ *
+ * The exact vector-Jacobian product of the weights for the fixed selection
+ * (the choice itself is not differentiated), computed in FP32 and rounded
+ * to ldt.  With u_j the selected scores, g_j = grad_weights, S = sum_l u_l,
+ * v_j = u_j/S, gbar = sum_l g_l v_l, and A_e the sum over the slots
+ * selecting e of a_j:
+ *   softmax:        grad_e = p_e * (A_e - sum_j u_j a_j), a_j = scale*g_j;
+ *   softmax, renormalised: grad_e = A_e with a_j = scale*v_j*(g_j - gbar)
+ *                   for a selected e, 0 for the others (the renormalised
+ *                   weights are the softmax over the selected logits);
+ *   sigmoid:        grad_e = s_e*(1-s_e)*A_e for a selected e, exactly 0 for
+ *                   the others, a_j = scale*g_j, or (scale/S)*(g_j - gbar)
+ *                   renormalised.
+ * NaN scores give NaN gradients as the arithmetic carries them.  An invalid
+ * index makes the whole gradient row NaN.  Limits as
+ * moe_selected_router_weights.
+ */
+int moe_selected_router_backward(const void* logits, int ldt, int64_t T,
+                                 int64_t E, const void* indices,
+                                 int index_type, int64_t top_k,
+                                 const float* grad_weights, int scoring,
+                                 int renormalize, float scale,
+                                 void* grad_logits, void* stream);
 
 /*
  * moe_set_timing_events - instrumentation for measuring each kernel.

@@ -1,7 +1,8 @@
 """Local Mixture-of-Experts forward for AMD Instinct MI355X (gfx950).
 
 route (FP32 softmax + top-k, or group-limited sigmoid routing) -> compact
-dispatch -> SwiGLU experts -> weighted combine, as hand-written HIP kernels
+dispatch -> SwiGLU experts -> weighted combine, plus the router weights of
+a fixed selection and their logits gradient, as hand-written HIP kernels
 behind the C ABI of libmoe.so (include/moe.h).  This package is the thin
 torch binding: the functions below have the names of the C entry points and
 only marshal arguments.
@@ -10,9 +11,11 @@ only marshal arguments.
 from .ops import (moe_combine, moe_dispatch, moe_dispatch_workspace_size,
                   moe_experts_forward, moe_forward, moe_forward_sigmoid_grouped,
                   moe_forward_workspace_size, moe_route,
-                  moe_route_sigmoid_grouped)
+                  moe_route_sigmoid_grouped, moe_selected_router_backward,
+                  moe_selected_router_weights)
 
 __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_experts_forward", "moe_combine", "moe_forward",
            "moe_forward_workspace_size", "moe_route_sigmoid_grouped",
-           "moe_forward_sigmoid_grouped"]
+           "moe_forward_sigmoid_grouped", "moe_selected_router_weights",
+           "moe_selected_router_backward"]

@@ -11,6 +11,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_F16, MOE_BF16 = 0, 1, 2
+MOE_IDX_U32, MOE_IDX_I32, MOE_IDX_I64 = 0, 1, 2
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_SHAPE",
           3: "MOE_ERR_DTYPE", 4: "MOE_ERR_UNSUPPORTED", 5: "MOE_ERR_HIP"}
 
@@ -40,6 +42,11 @@ SIGNATURES = {
                                            _I64, _I64, _I64, _I64, _I64, _INT,
                                            _INT, _F32, _P, _P, _P, _P, _P,
                                            _SZ, _P]),
+    "moe_selected_router_weights": (_INT, [_P, _INT, _I64, _I64, _P, _INT,
+                                           _I64, _INT, _INT, _F32, _P, _P]),
+    "moe_selected_router_backward": (_INT, [_P, _INT, _I64, _I64, _P, _INT,
+                                            _I64, _P, _INT, _INT, _F32, _P,
+                                            _P]),
     "moe_set_timing_events": (_INT, [_P, _INT]),
     "moe_status_string": (ctypes.c_char_p, [_INT]),
     "moe_last_error": (ctypes.c_char_p, []),

@@ -33,6 +33,22 @@ hipError_t launch_route_sigmoid(const void* logits, int ldt, const float* bias,
                                 const GroupRouting& o, uint32_t* idx, void* w,
                                 hipStream_t st);
 
+// Router weights of a fixed selection and their logits gradient.  Index
+// element types (values as in moe.h's moe_index_type):
+enum IndexType { IDX_U32 = 0, IDX_I32 = 1, IDX_I64 = 2 };
+// 1 <= k <= min(E, 64); sigmoid selects the scoring (else softmax).
+hipError_t launch_selected_router_weights(const void* logits, int ldt,
+                                          int64_t T, int E, const void* ind,
+                                          int it, int k, int sigmoid,
+                                          int renorm, float scale, float* w,
+                                          hipStream_t st);
+hipError_t launch_selected_router_backward(const void* logits, int ldt,
+                                           int64_t T, int E, const void* ind,
+                                           int it, int k, const float* grad_w,
+                                           int sigmoid, int renorm,
+                                           float scale, void* grad_x,
+                                           hipStream_t st);
+
 // ---- dispatch --------------------------------------------------------------
 // Scratch layout: a table of per-chunk expert counts [nchunks][E+1] u32,
 // reused in place for the per-chunk row bases.

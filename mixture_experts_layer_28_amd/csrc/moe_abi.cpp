@@ -104,6 +104,27 @@ int check_route_sigmoid(const void* logits, int ldt, int64_t T, int64_t E,
   return MOE_OK;
 }
 
+int check_router_weights(const char* f, const void* logits, int ldt,
+                         int64_t T, int64_t E, const void* ind, int it,
+                         int64_t k, int scoring, float scale, const void* a,
+                         const void* b) {
+  if (!valid_dtype(ldt)) return fail(MOE_ERR_DTYPE, "%s: unknown logits dtype %d", f, ldt);
+  if (it != MOE_IDX_U32 && it != MOE_IDX_I32 && it != MOE_IDX_I64)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown index type %d", f, it);
+  if (scoring != MOE_SCORE_SOFTMAX && scoring != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown scoring %d", f, scoring);
+  if (T < 0) return fail(MOE_ERR_SHAPE, "%s: T must be >= 0", f);
+  if (E < 1 || E > INT32_MAX) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in 1..2^31-1", f);
+  if (k < 1 || k > E || k > kMaxSigmoidK)
+    return fail(MOE_ERR_INVALID_ARG, "%s: top_k must satisfy 1 <= top_k <= min(E, 64)", f);
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(MOE_ERR_INVALID_ARG, "%s: scale must be finite and positive", f);
+  int64_t n;
+  if (!mul_ok(T, k, &n) || !bytes_ok(T, k, 8) || !bytes_ok(T, E, 4))
+    return fail(MOE_ERR_SHAPE, "%s: sizes overflow", f);
+  if (T > 0 && (!logits || !ind || !a || !b)) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", f);
+  return MOE_OK;
+}
+
 moe::GroupRouting group_routing(int64_t E, int64_t groups, int64_t sel,
                                 int top_two, int renorm, float scale) {
   moe::GroupRouting o;
@@ -442,6 +463,44 @@ int moe_forward_sigmoid_grouped(const void* x, int dt, const void* logits,
         return moe::launch_route_sigmoid(logits, ldt, bias, T, (int)E,
                                          (int)top_k, o, idx, w, st);
       });
+}
+
+int moe_selected_router_weights(const void* logits, int ldt, int64_t T,
+                                int64_t E, const void* indices,
+                                int index_type, int64_t top_k, int scoring,
+                                int renormalize, float scale, float* weights,
+                                void* stream) {
+  const int s = check_router_weights("moe_selected_router_weights", logits,
+                                     ldt, T, E, indices, index_type, top_k,
+                                     scoring, scale, weights, weights);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  return hip_status(moe::launch_selected_router_weights(
+                        logits, ldt, T, (int)E, indices, index_type,
+                        (int)top_k, scoring == MOE_SCORE_SIGMOID,
+                        renormalize ? 1 : 0, scale, weights,
+                        (hipStream_t)stream),
+                    "moe_selected_router_weights");
+}
+
+int moe_selected_router_backward(const void* logits, int ldt, int64_t T,
+                                 int64_t E, const void* indices,
+                                 int index_type, int64_t top_k,
+                                 const float* grad_weights, int scoring,
+                                 int renormalize, float scale,
+                                 void* grad_logits, void* stream) {
+  const int s = check_router_weights("moe_selected_router_backward", logits,
+                                     ldt, T, E, indices, index_type, top_k,
+                                     scoring, scale, grad_weights,
+                                     grad_logits);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  return hip_status(moe::launch_selected_router_backward(
+                        logits, ldt, T, (int)E, indices, index_type,
+                        (int)top_k, grad_weights,
+                        scoring == MOE_SCORE_SIGMOID, renormalize ? 1 : 0,
+                        scale, grad_logits, (hipStream_t)stream),
+                    "moe_selected_router_backward");
 }
 
 }  // extern "C"

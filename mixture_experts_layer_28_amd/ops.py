@@ -250,7 +250,70 @@ def moe_forward_sigmoid_grouped(x, logits, w_gate, w_up, w_down, top_k,
     return out
 
 
+_INDEX_TYPES = {"u32": (_lib.MOE_IDX_U32, 4), "i32": (_lib.MOE_IDX_I32, 4),
+                "i64": (_lib.MOE_IDX_I64, 8)}
+_SCORING = {"softmax": _lib.MOE_SCORE_SOFTMAX,
+            "sigmoid": _lib.MOE_SCORE_SIGMOID}
+
+
+def _router_indices(indices, T, index_type):
+    """indices [T,k] of int32 (read as "i32", or "u32" for the uint32 bits
+    moe_route writes), int64 ("i64") or uint32 ("u32")."""
+    if index_type is None:
+        index_type = {torch.int32: "i32", torch.int64: "i64",
+                      torch.uint32: "u32"}.get(indices.dtype)
+        if index_type is None:
+            raise TypeError("indices must be int32, int64 or uint32")
+    code, size = _INDEX_TYPES[index_type]
+    if indices.dim() != 2 or indices.shape[0] != T:
+        raise ValueError("indices must be [T, top_k]")
+    if indices.element_size() != size or indices.is_floating_point():
+        raise TypeError("indices of type %s need %d-byte integer elements"
+                        % (index_type, size))
+    return code
+
+
+def moe_selected_router_weights(logits, indices, scoring="softmax",
+                                renormalize=False, scale=1.0,
+                                index_type=None, out=None):
+    """FP32 router weights [T,k] of the experts ``indices`` [T,k] selects
+    (softmax or sigmoid scores, optional renormalisation, scale)."""
+    logits, indices = _c(logits), _c(indices)
+    dev = _dev(logits, indices)
+    T, E = logits.shape
+    it = _router_indices(indices, T, index_type)
+    k = indices.shape[1]
+    out = _out(out, (T, k), torch.float32, dev, "weights")
+    check(lib().moe_selected_router_weights(
+        _p(logits), _dt(logits, "logits"), T, E, _p(indices), it, k,
+        _SCORING[scoring], int(bool(renormalize)), float(scale), _p(out),
+        _stream(dev)))
+    return out
+
+
+def moe_selected_router_backward(logits, indices, grad_weights,
+                                 scoring="softmax", renormalize=False,
+                                 scale=1.0, index_type=None, out=None):
+    """The logits gradient [T,E] (logits dtype) of
+    moe_selected_router_weights for FP32 ``grad_weights`` [T,k]."""
+    logits, indices = _c(logits), _c(indices)
+    grad_weights = _c(grad_weights)
+    dev = _dev(logits, indices, grad_weights)
+    T, E = logits.shape
+    it = _router_indices(indices, T, index_type)
+    k = indices.shape[1]
+    if grad_weights.dtype != torch.float32 or grad_weights.shape != (T, k):
+        raise ValueError("grad_weights must be a float32 [T, top_k] tensor")
+    out = _out(out, (T, E), logits.dtype, dev, "grad_logits")
+    check(lib().moe_selected_router_backward(
+        _p(logits), _dt(logits, "logits"), T, E, _p(indices), it, k,
+        _p(grad_weights), _SCORING[scoring], int(bool(renormalize)),
+        float(scale), _p(out), _stream(dev)))
+    return out
+
+
 __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_experts_forward", "moe_combine", "moe_forward",
            "moe_forward_workspace_size", "moe_route_sigmoid_grouped",
-           "moe_forward_sigmoid_grouped", "_lib"]
+           "moe_forward_sigmoid_grouped", "moe_selected_router_weights",
+           "moe_selected_router_backward", "_lib"]

@@ -228,3 +228,52 @@ def test_forward_sigmoid_rejects():
     a = list(args)
     a[5] = 0         # T = 0: nothing to do
     assert L.moe_forward_sigmoid_grouped(*a) == 0
+
+
+# moe_selected_router_weights(logits, ldt, T, E, indices, index_type, top_k,
+#                             scoring, renormalize, scale, weights, stream)
+_RW = [FAKE, 2, 16, 64, FAKE, 0, 8, 0, 1, 1.0, FAKE, None]
+
+
+@pytest.mark.parametrize("i,v,status", [
+    (1, 9, 3),             # bad logits dtype
+    (5, 3, 1),             # unknown index type
+    (7, 2, 1),             # unknown scoring
+    (2, -1, 2),            # T < 0
+    (3, 0, 1),             # E = 0
+    (6, 0, 1),             # top_k = 0
+    (6, 65, 1),            # top_k > 64
+    (9, 0.0, 1),           # scale
+    (9, float("nan"), 1),
+    (0, None, 1),          # null logits
+    (4, None, 1),          # null indices
+    (10, None, 1),         # null weights
+])
+def test_router_weights_rejects(i, v, status):
+    a = list(_RW)
+    a[i] = v
+    assert _lib.lib().moe_selected_router_weights(*a) == status, (i, v)
+    assert _last()
+
+
+def test_router_weights_limits():
+    L = _lib.lib()
+    a = list(_RW)
+    a[3], a[6] = 4, 5        # top_k > E
+    assert L.moe_selected_router_weights(*a) == 1 and "top_k" in _last()
+    a = list(_RW)
+    a[2], a[0], a[4], a[10] = 0, None, None, None   # T = 0: nothing to do
+    assert L.moe_selected_router_weights(*a) == 0 and _last() == ""
+
+
+def test_router_backward_rejects():
+    L = _lib.lib()
+    args = [FAKE, 2, 16, 64, FAKE, 2, 8, FAKE, 1, 0, 2.5, FAKE, None]
+    for i, v, st in [(7, None, 1), (11, None, 1), (5, 7, 1), (8, 5, 1),
+                     (6, 65, 1), (10, -1.0, 1), (1, 4, 3)]:
+        a = list(args)
+        a[i] = v
+        assert L.moe_selected_router_backward(*a) == st, (i, v)
+    a = list(args)
+    a[2] = 0
+    assert L.moe_selected_router_backward(*a) == 0
