@@ -34,10 +34,18 @@ Parity status of each function (what pins it is listed in the test files
                               pinned (torch autograd in float64, finite
                               differences, closed forms, invariants)
 
+* ``backward.experts_forward_training``, ``combine_backward``,
+  ``experts_backward``, ``dispatch_backward``
+                              pinned (torch autograd in float64 through the
+                              whole layer, finite differences, adjointness
+                              of dispatch and combine, training forward equal
+                              to the inference forward)
+
 ``grouped`` follows section 10 of the same guide (group-limited sigmoid
 routing) and the experts page's ``forward_sigmoid_grouped``;
 ``router_weights`` follows section 12 (router weights of a fixed selection
-and their logits gradient).
+and their logits gradient); ``backward`` follows section 12's backward chain
+and the experts page's training forward and expert backward.
 """
 
-from . import fp, grouped, moe, router_weights  # noqa: F401
+from . import backward, fp, grouped, moe, router_weights  # noqa: F401
