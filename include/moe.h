@@ -313,6 +313,123 @@ int moe_selected_router_backward(const void* logits, int ldt, int64_t T,
                                  void* grad_logits, void* stream);
 
 /*
+ * First-order training (guide, section 12; experts page,
+ * forward_dispatched_training and ExpertTrainingCache::backward).  The
+ * backward chain, after a forward that used moe_dispatch and
+ * moe_experts_forward_training (and FP32 routing weights, e.g. from
+ * moe_selected_router_weights):
+ *   moe_combine_backward -> moe_experts_backward -> moe_dispatch_backward
+ *   -> moe_selected_router_backward (logits gradient from the weight
+ *   gradient).
+ * Tensors the chain materialises are rounded to their dtype once; weight
+ * gradients are FP32.
+ */
+
+/*
+ * moe_experts_forward_training - moe_experts_forward that keeps what the
+ * expert backward needs (experts page, forward_dispatched_training).
+ *
+ *   xd, w_gate, w_up, w_down, offsets   as moe_experts_forward
+ *   gate [N,I] dt   output: xd . w_gate[e]^T, FP32 accumulation, rounded
+ *   up   [N,I] dt   output: xd . w_up[e]^T, rounded
+ *   act  [N,I] dt   output: SiLU(gate) * up (FP32 from the stored gate and
+ *                   up), rounded
+ *   y    [N,H] dt   output: act . w_down[e]^T, rounded
+ * Rows in [offsets[E], N) get zeros.  Limits as moe_experts_forward.
+ */
+int moe_experts_forward_training(const void* xd, int dt, int64_t N,
+                                 int64_t H, int64_t I, int64_t E,
+                                 const void* w_gate, const void* w_up,
+                                 const void* w_down, const uint32_t* offsets,
+                                 void* gate, void* up, void* act, void* y,
+                                 void* stream);
+
+/*
+ * moe_combine_backward - gradients of moe_combine (guide, section 12,
+ * step 1).
+ *
+ *   y            [N,H]      dt      expert output rows (forward input)
+ *   weights      [T,top_k]  wdt     routing weights (forward input)
+ *   token_row    [T,top_k]  uint32  the dispatch mapping
+ *   grad_out     [T,H]      dt      dL/dout
+ *   grad_expert  [N,H]      dt      output: row token_row[t,j] gets
+ *                                   weights[t,j] * grad_out[t] (FP32,
+ *                                   rounded); rows no slot maps are not
+ *                                   written (moe_dispatch maps every row)
+ *   grad_weights [T,top_k]  float32 output: grad_out[t] . y[token_row[t,j]]
+ *                                   in FP32
+ * A token_row value >= N gets a NaN weight gradient and writes no row.
+ * top_k <= 8192.
+ */
+int moe_combine_backward(const void* y, int dt, int64_t N, int64_t T,
+                         int64_t H, int64_t top_k, const void* weights,
+                         int wdt, const uint32_t* token_row,
+                         const void* grad_out, void* grad_expert,
+                         float* grad_weights, void* stream);
+
+/*
+ * moe_experts_backward_workspace_size - bytes of scratch
+ * moe_experts_backward needs (one transposed weight tensor, three [N,I] and
+ * two [N,H] intermediates).  Returns 0 for invalid arguments.
+ */
+size_t moe_experts_backward_workspace_size(int64_t N, int64_t H, int64_t I,
+                                           int64_t E, int dt);
+
+/*
+ * moe_experts_backward - the expert backward (guide, section 12, step 2;
+ * experts page, ExpertTrainingCache::backward_with_strategy).
+ *
+ *   xd, w_gate, w_up, w_down, offsets   the forward's inputs
+ *   gate, up, act [N,I] dt   the training forward's cache
+ *   grad_y      [N,H]   dt       dL/dy (from moe_combine_backward)
+ *   grad_xd     [N,H]   dt       output: dL/dxd
+ *   grad_w_gate [E,I,H] float32  output
+ *   grad_w_up   [E,I,H] float32  output
+ *   grad_w_down [E,H,I] float32  output
+ *   workspace   moe_experts_backward_workspace_size(N,H,I,E,dt) bytes,
+ *               256-byte aligned.  It holds, in this order, each part at
+ *               the next 256-byte aligned offset: one transposed weight
+ *               tensor (E*H*I elements of dt), then dact, dgate_raw,
+ *               dup_raw [N,I] and the two input-gradient halves
+ *               round(dgate_raw . w_gate[e]), round(dup_raw . w_up[e])
+ *               [N,H], all dt; after the call these five hold the
+ *               intermediates named below.
+ *
+ * In the experts page's order, each intermediate rounded to dt:
+ * dact = grad_y . w_down[e]; dgate_raw = dact * up * s * (1 + gate*(1-s)),
+ * dup_raw = dact * gate * s with s = sigmoid(gate); grad_xd =
+ * round(round(dgate_raw . w_gate[e]) + round(dup_raw . w_up[e])).  Weight
+ * gradients, FP32 sums over each expert's rows: grad_w_down[e] =
+ * grad_y^T . act, grad_w_gate[e] = dgate_raw^T . xd, grad_w_up[e] =
+ * dup_raw^T . xd; an expert with no rows gets zeros.  Rows in
+ * [offsets[E], N) get grad_xd = 0.  Limits as moe_experts_forward.
+ */
+int moe_experts_backward(const void* xd, int dt, int64_t N, int64_t H,
+                         int64_t I, int64_t E, const void* w_gate,
+                         const void* w_up, const void* w_down,
+                         const uint32_t* offsets, const void* gate,
+                         const void* up, const void* act, const void* grad_y,
+                         void* grad_xd, float* grad_w_gate, float* grad_w_up,
+                         float* grad_w_down, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * moe_dispatch_backward - the gradient of moe_dispatch (guide, section 12,
+ * step 3): grad_x[t] = sum over slots j, in slot order and in FP32, of
+ * grad_xd[token_row[t,j]], rounded once to dt; the routing weights are not
+ * applied again.
+ *
+ *   grad_xd   [N,H]      dt      dL/dxd
+ *   token_row [T,top_k]  uint32  the dispatch mapping
+ *   grad_x    [T,H]      dt      output
+ * A token_row value >= N makes that token's gradient NaN.  top_k <= 8192.
+ */
+int moe_dispatch_backward(const void* grad_xd, int dt, int64_t N, int64_t T,
+                          int64_t H, int64_t top_k,
+                          const uint32_t* token_row, void* grad_x,
+                          void* stream);
+
+/*
  * moe_set_timing_events - instrumentation for measuring each kernel.
  *
  * events: `count` hipEvent_t handles created by the caller (hipEventCreate),

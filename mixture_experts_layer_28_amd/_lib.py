@@ -47,6 +47,18 @@ SIGNATURES = {
     "moe_selected_router_backward": (_INT, [_P, _INT, _I64, _I64, _P, _INT,
                                             _I64, _P, _INT, _INT, _F32, _P,
                                             _P]),
+    "moe_experts_forward_training": (_INT, [_P, _INT, _I64, _I64, _I64, _I64,
+                                            _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P]),
+    "moe_combine_backward": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P,
+                                    _INT, _P, _P, _P, _P, _P]),
+    "moe_experts_backward_workspace_size": (_SZ, [_I64, _I64, _I64, _I64,
+                                                  _INT]),
+    "moe_experts_backward": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _SZ, _P]),
+    "moe_dispatch_backward": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P,
+                                     _P]),
     "moe_set_timing_events": (_INT, [_P, _INT]),
     "moe_status_string": (ctypes.c_char_p, [_INT]),
     "moe_last_error": (ctypes.c_char_p, []),

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["moe_abi.cpp", "route.hip", "route_sigmoid.hip", "dispatch.hip",
-           "gemm.hip", "gemm_big.hip", "combine.hip", "router_weights.hip"]
+           "gemm.hip", "gemm_big.hip", "combine.hip", "router_weights.hip",
+           "backward.hip"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature",
                 "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -1,0 +1,426 @@
+// Kernels of the first-order MoE training path.
+//
+// Contract: ruDNN user guide (RUDA docs, German edition), section 12
+// "first-order MoE training" (combine backward -> expert backward ->
+// dispatch backward -> router backward), and the experts page (docs.rs
+// "ruDNN 0.1.25 source, src/moe/experts.rs": forward_dispatched_training,
+// ExpertTrainingCache::backward_with_strategy), which fixes what the
+// training forward keeps (raw gate and up products, the activation) and the
+// expert backward's order: the down projection's backward, a SwiGLU
+// backward, the gate and up projections' backwards, and the sum of their
+// input gradients.  Every tensor that order materialises is rounded to the
+// storage dtype; weight gradients are FP32.
+//
+// The products reuse the grouped NT GEMMs of the forward:
+//   gate = xd . Wg^T, up = xd . Wu^T            (training forward)
+//   dact = dy . Wd        = NT(dy, Wd^T)        (Wd^T [E,I,H], transposed)
+//   dxg  = dg . Wg        = NT(dg, Wg^T)        (Wg^T [E,H,I], transposed)
+//   dxu  = du . Wu        = NT(du, Wu^T)
+// The transposes cost one read and one write of a weight tensor each; the
+// NT kernels then run at their forward speed.  The weight gradients are
+// "TN" products over each expert's rows,
+//   ddown[e] = dy_e^T . act_e,  dgate[e] = dg_e^T . xd_e,  dup[e] = du_e^T . xd_e,
+// computed here by an LDS-tiled FP32 kernel (tn_kernel).  Elementwise
+// kernels do the SwiGLU forward and backward and the final add.
+
+#include "device_common.h"
+#include "gemm_common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int64_t kMaxGrid = 1 << 20;  // grid-stride loops beyond this
+
+inline unsigned capped(int64_t blocks) {
+  return (unsigned)(blocks < kMaxGrid ? (blocks > 0 ? blocks : 1) : kMaxGrid);
+}
+
+// ---- transpose: out[e][c][r] = in[e][r][c] ---------------------------------
+template <typename W>
+__global__ __launch_bounds__(256) void transpose_kernel(
+    const W* __restrict__ in, W* __restrict__ out, int64_t E, int64_t R,
+    int64_t C) {
+  __shared__ W tile[64][65];
+  const int64_t nr = (R + 63) / 64, nc = (C + 63) / 64;
+  const int64_t total = E * nr * nc;
+  const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+  for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    const int64_t e = b / (nr * nc);
+    const int64_t rb = (b / nc) % nr, cb = b % nc;
+    const W* src = in + e * R * C;
+    W* dst = out + e * R * C;
+    for (int i = ty; i < 64; i += 4) {
+      const int64_t r = rb * 64 + i, c = cb * 64 + tx;
+      if (r < R && c < C) tile[i][tx] = src[r * C + c];
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+      const int64_t c = cb * 64 + i, r = rb * 64 + tx;
+      if (r < R && c < C) dst[c * R + r] = tile[tx][i];
+    }
+    __syncthreads();
+  }
+}
+
+// ---- elementwise -----------------------------------------------------------
+// act = SiLU(g) * u from the stored (rounded) g and u, as the forward's
+// fused epilogue computes it.
+template <int D>
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(
+    const typename Storage<D>::T* __restrict__ g,
+    const typename Storage<D>::T* __restrict__ u,
+    typename Storage<D>::T* __restrict__ a, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    a[i] = from_f32<D>(silu_mul(to_f32<D>(g[i]), to_f32<D>(u[i])));
+}
+
+// SwiGLU backward of a = SiLU(g) * u, s = sigmoid(g):
+//   dg = da * u * s * (1 + g * (1 - s)),  du = da * g * s
+template <int D>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(
+    const typename Storage<D>::T* __restrict__ g,
+    const typename Storage<D>::T* __restrict__ u,
+    const typename Storage<D>::T* __restrict__ da,
+    typename Storage<D>::T* __restrict__ dg,
+    typename Storage<D>::T* __restrict__ du, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256) {
+    const float gv = to_f32<D>(g[i]), uv = to_f32<D>(u[i]);
+    const float d = to_f32<D>(da[i]);
+    const float s = 1.0f / (1.0f + expf(-gv));
+    dg[i] = from_f32<D>(d * uv * s * (1.0f + gv * (1.0f - s)));
+    du[i] = from_f32<D>(d * gv * s);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void add_kernel(
+    const typename Storage<D>::T* __restrict__ a,
+    const typename Storage<D>::T* __restrict__ b,
+    typename Storage<D>::T* __restrict__ c, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    c[i] = from_f32<D>(to_f32<D>(a[i]) + to_f32<D>(b[i]));
+}
+
+// ---- combine backward ------------------------------------------------------
+// One workgroup (4 waves) per token; wave v takes slots v, v + 4, ...  For
+// slot j with row r = token_row[t, j]: dexpert[r] = w[t, j] * dout[t]
+// (rounded to the dtype) and dweights[t, j] = dout[t] . y[r] in FP32.  A
+// row id >= N is not touched and gets a NaN weight gradient.  NV elements
+// per load (16-byte vectors when the rows allow, else 1).
+template <int D, int WD, int NV>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const typename Storage<D>::T* __restrict__ y, int64_t N, int64_t T,
+    int64_t H, int k, const typename Storage<WD>::T* __restrict__ w,
+    const uint32_t* __restrict__ token_row,
+    const typename Storage<D>::T* __restrict__ dout,
+    typename Storage<D>::T* __restrict__ dexp, float* __restrict__ dw) {
+  using S = typename Storage<D>::T;
+  const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
+  const int64_t vpr = H / NV;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const S* go = dout + t * H;
+    for (int j = wv; j < k; j += 4) {
+      const uint32_t r = token_row[t * k + j];
+      const float wt = to_f32<WD>(w[t * k + j]);
+      float dot = 0.0f;
+      if (r < (uint64_t)N) {
+        const S* yr = y + (int64_t)r * H;
+        S* dr = dexp + (int64_t)r * H;
+        for (int64_t v = lane; v < vpr; v += 64) {
+          S a[NV], b[NV], o[NV];
+          if constexpr (NV * sizeof(S) == 16) {
+            *(u32x4*)a = *(const u32x4*)(go + v * NV);
+            *(u32x4*)b = *(const u32x4*)(yr + v * NV);
+          } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+              a[i] = go[v * NV + i];
+              b[i] = yr[v * NV + i];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const float gv = to_f32<D>(a[i]);
+            dot = fmaf(gv, to_f32<D>(b[i]), dot);
+            o[i] = from_f32<D>(wt * gv);
+          }
+          if constexpr (NV * sizeof(S) == 16) {
+            *(u32x4*)(dr + v * NV) = *(const u32x4*)o;
+          } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) dr[v * NV + i] = o[i];
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+      if (lane == 0) dw[t * k + j] = r < (uint64_t)N ? dot : __builtin_nanf("");
+    }
+  }
+}
+
+// ---- weight gradients: C[e] = A_e^T . B_e over the rows of segment e -------
+// A [N,M], B [N,NC] (dtype), C [E,M,NC] FP32.  64 x 64 output tile per
+// workgroup, 4 x 4 per thread, K (rows) in steps of 16 staged in LDS as
+// FP32.  An empty segment writes zeros.
+template <int D>
+__global__ __launch_bounds__(256) void tn_kernel(
+    const typename Storage<D>::T* __restrict__ A,
+    const typename Storage<D>::T* __restrict__ B,
+    const uint32_t* __restrict__ offsets, int64_t N, int E, int64_t M,
+    int64_t NC, float* __restrict__ C) {
+  constexpr int BK = 16;
+  __shared__ float As[BK][64 + 4];
+  __shared__ float Bs[BK][64 + 4];
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int64_t nm = (M + 63) / 64, nn = (NC + 63) / 64;
+  const int64_t total = (int64_t)E * nm * nn;
+  for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    const int e = (int)(b / (nm * nn));
+    const int64_t m0 = ((b / nn) % nm) * 64, c0 = (b % nn) * 64;
+    int64_t hi = offsets[e + 1];
+    hi = hi < N ? hi : N;
+    int64_t lo = offsets[e];
+    lo = lo < hi ? lo : hi;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int64_t r0 = lo; r0 < hi; r0 += BK) {
+      // 16 rows x 64 columns of each operand, 4 per thread
+      const int lr = threadIdx.x / 16, lc = (threadIdx.x % 16) * 4;
+      const int64_t r = r0 + lr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t m = m0 + lc + q, c = c0 + lc + q;
+        As[lr][lc + q] = r < hi && m < M ? to_f32<D>(A[r * M + m]) : 0.0f;
+        Bs[lr][lc + q] = r < hi && c < NC ? to_f32<D>(B[r * NC + c]) : 0.0f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < BK; ++kk) {
+        float a[4], bb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bb[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], bb[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+    float* ce = C + (int64_t)e * M * NC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + ty * 4 + i;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t c = c0 + tx * 4 + j;
+        if (c < NC) ce[m * NC + c] = acc[i][j];
+      }
+    }
+  }
+}
+
+template <typename W>
+hipError_t transpose(const void* in, void* out, int64_t E, int64_t R,
+                     int64_t C, hipStream_t st) {
+  const int64_t blocks = E * ((R + 63) / 64) * ((C + 63) / 64);
+  hipLaunchKernelGGL((transpose_kernel<W>), dim3(capped(blocks)), dim3(256), 0,
+                     st, (const W*)in, (W*)out, E, R, C);
+  return hipGetLastError();
+}
+
+hipError_t transpose_dt(const void* in, int dt, void* out, int64_t E,
+                        int64_t R, int64_t C, hipStream_t st) {
+  if (dt == DT_F32) return transpose<uint32_t>(in, out, E, R, C, st);
+  return transpose<uint16_t>(in, out, E, R, C, st);
+}
+
+template <int D>
+hipError_t tn(const void* A, const void* B, const uint32_t* offsets,
+              int64_t N, int E, int64_t M, int64_t NC, float* C,
+              hipStream_t st) {
+  using S = typename Storage<D>::T;
+  const int64_t blocks = (int64_t)E * ((M + 63) / 64) * ((NC + 63) / 64);
+  hipLaunchKernelGGL((tn_kernel<D>), dim3(capped(blocks)), dim3(256), 0, st,
+                     (const S*)A, (const S*)B, offsets, N, E, M, NC, C);
+  return hipGetLastError();
+}
+
+hipError_t tn_dt(const void* A, int dt, const void* B,
+                 const uint32_t* offsets, int64_t N, int E, int64_t M,
+                 int64_t NC, float* C, hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return tn<DT_F32>(A, B, offsets, N, E, M, NC, C, st);
+    case DT_F16: return tn<DT_F16>(A, B, offsets, N, E, M, NC, C, st);
+    default: return tn<DT_BF16>(A, B, offsets, N, E, M, NC, C, st);
+  }
+}
+
+template <int D>
+hipError_t elementwise_fwd(const void* g, const void* u, void* a, int64_t n,
+                           hipStream_t st) {
+  using S = typename Storage<D>::T;
+  hipLaunchKernelGGL((swiglu_fwd_kernel<D>), dim3(capped((n + 255) / 256)),
+                     dim3(256), 0, st, (const S*)g, (const S*)u, (S*)a, n);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t elementwise_bwd(const void* g, const void* u, const void* da,
+                           void* dg, void* du, int64_t n, hipStream_t st) {
+  using S = typename Storage<D>::T;
+  hipLaunchKernelGGL((swiglu_bwd_kernel<D>), dim3(capped((n + 255) / 256)),
+                     dim3(256), 0, st, (const S*)g, (const S*)u,
+                     (const S*)da, (S*)dg, (S*)du, n);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t elementwise_add(const void* a, const void* b, void* c, int64_t n,
+                           hipStream_t st) {
+  using S = typename Storage<D>::T;
+  hipLaunchKernelGGL((add_kernel<D>), dim3(capped((n + 255) / 256)),
+                     dim3(256), 0, st, (const S*)a, (const S*)b, (S*)c, n);
+  return hipGetLastError();
+}
+
+#define MOE_BY_DT(dt, fn, ...)                                     \
+  ((dt) == DT_F32 ? fn<DT_F32>(__VA_ARGS__)                        \
+                  : (dt) == DT_F16 ? fn<DT_F16>(__VA_ARGS__)       \
+                                   : fn<DT_BF16>(__VA_ARGS__))
+
+template <int D, int WD>
+hipError_t combine_bwd(const void* y, int64_t N, int64_t T, int64_t H, int k,
+                       const void* w, const uint32_t* token_row,
+                       const void* dout, void* dexp, float* dw,
+                       hipStream_t st) {
+  using S = typename Storage<D>::T;
+  using SW = typename Storage<WD>::T;
+  constexpr int NV = 16 / sizeof(S);
+  const uintptr_t al = (uintptr_t)y | (uintptr_t)dout | (uintptr_t)dexp;
+  const dim3 grid(capped(T));
+  if (H % NV == 0 && al % 16 == 0)
+    hipLaunchKernelGGL((combine_bwd_kernel<D, WD, NV>), grid, dim3(256), 0, st,
+                       (const S*)y, N, T, H, k, (const SW*)w, token_row,
+                       (const S*)dout, (S*)dexp, dw);
+  else
+    hipLaunchKernelGGL((combine_bwd_kernel<D, WD, 1>), grid, dim3(256), 0, st,
+                       (const S*)y, N, T, H, k, (const SW*)w, token_row,
+                       (const S*)dout, (S*)dexp, dw);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t combine_bwd_w(const void* y, int64_t N, int64_t T, int64_t H,
+                         int k, const void* w, int wdt,
+                         const uint32_t* token_row, const void* dout,
+                         void* dexp, float* dw, hipStream_t st) {
+  switch (wdt) {
+    case DT_F32: return combine_bwd<D, DT_F32>(y, N, T, H, k, w, token_row, dout, dexp, dw, st);
+    case DT_F16: return combine_bwd<D, DT_F16>(y, N, T, H, k, w, token_row, dout, dexp, dw, st);
+    default: return combine_bwd<D, DT_BF16>(y, N, T, H, k, w, token_row, dout, dexp, dw, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_experts_forward_training(
+    const void* xd, int dt, int64_t N, int64_t H, int64_t I, int E,
+    const void* w_gate, const void* w_up, const void* w_down,
+    const uint32_t* offsets, void* gate, void* up, void* act, void* y,
+    hipStream_t st) {
+  hipError_t err = launch_grouped_nt(xd, dt, N, H, w_gate, I, E, offsets,
+                                     gate, st);
+  if (err == hipSuccess)
+    err = launch_grouped_nt(xd, dt, N, H, w_up, I, E, offsets, up, st);
+  if (err == hipSuccess)
+    err = MOE_BY_DT(dt, elementwise_fwd, gate, up, act, N * I, st);
+  if (err == hipSuccess)
+    err = launch_grouped_nt(act, dt, N, I, w_down, H, E, offsets, y, st);
+  return err;
+}
+
+hipError_t launch_combine_backward(const void* y, int dt, int64_t N,
+                                   int64_t T, int64_t H, int k,
+                                   const void* w, int wdt,
+                                   const uint32_t* token_row,
+                                   const void* dout, void* dexp, float* dw,
+                                   hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return combine_bwd_w<DT_F32>(y, N, T, H, k, w, wdt, token_row, dout, dexp, dw, st);
+    case DT_F16: return combine_bwd_w<DT_F16>(y, N, T, H, k, w, wdt, token_row, dout, dexp, dw, st);
+    default: return combine_bwd_w<DT_BF16>(y, N, T, H, k, w, wdt, token_row, dout, dexp, dw, st);
+  }
+}
+
+ExpertsBackwardLayout experts_backward_layout(int64_t N, int64_t H,
+                                              int64_t I, int64_t E, int dt) {
+  const size_t s = dt == DT_F32 ? 4 : 2;
+  ExpertsBackwardLayout L;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at = (at + bytes + 255) & ~size_t(255);
+    return here;
+  };
+  L.wt = take((size_t)E * H * I * s);
+  L.dact = take((size_t)N * I * s);
+  L.dg = take((size_t)N * I * s);
+  L.du = take((size_t)N * I * s);
+  L.dxg = take((size_t)N * H * s);
+  L.dxu = take((size_t)N * H * s);
+  L.total = at;
+  return L;
+}
+
+hipError_t launch_experts_backward(
+    const void* xd, int dt, int64_t N, int64_t H, int64_t I, int E,
+    const void* w_gate, const void* w_up, const void* w_down,
+    const uint32_t* offsets, const void* gate, const void* up,
+    const void* act, const void* dy, void* dxd, float* dwg, float* dwu,
+    float* dwd, void* workspace, hipStream_t st) {
+  const ExpertsBackwardLayout L = experts_backward_layout(N, H, I, E, dt);
+  char* ws = (char*)workspace;
+  void* wt = ws + L.wt;
+  void* dact = ws + L.dact;
+  void* dg = ws + L.dg;
+  void* du = ws + L.du;
+  void* dxg = ws + L.dxg;
+  void* dxu = ws + L.dxu;
+  // down projection: input gradient through Wd^T [E,I,H], weight gradient
+  hipError_t err = transpose_dt(w_down, dt, wt, E, H, I, st);
+  if (err == hipSuccess)
+    err = launch_grouped_nt(dy, dt, N, H, wt, I, E, offsets, dact, st);
+  if (err == hipSuccess)
+    err = tn_dt(dy, dt, act, offsets, N, E, H, I, dwd, st);
+  // SwiGLU backward
+  if (err == hipSuccess)
+    err = MOE_BY_DT(dt, elementwise_bwd, gate, up, dact, dg, du, N * I, st);
+  // gate and up projections: input gradients through Wg^T, Wu^T [E,H,I]
+  // (one transposed copy at a time), weight gradients, then the sum
+  if (err == hipSuccess) err = transpose_dt(w_gate, dt, wt, E, I, H, st);
+  if (err == hipSuccess)
+    err = launch_grouped_nt(dg, dt, N, I, wt, H, E, offsets, dxg, st);
+  if (err == hipSuccess) err = transpose_dt(w_up, dt, wt, E, I, H, st);
+  if (err == hipSuccess)
+    err = launch_grouped_nt(du, dt, N, I, wt, H, E, offsets, dxu, st);
+  if (err == hipSuccess)
+    err = MOE_BY_DT(dt, elementwise_add, dxg, dxu, dxd, N * H, st);
+  if (err == hipSuccess)
+    err = tn_dt(dg, dt, xd, offsets, N, E, I, H, dwg, st);
+  if (err == hipSuccess)
+    err = tn_dt(du, dt, xd, offsets, N, E, I, H, dwu, st);
+  return err;
+}
+
+}  // namespace moe

@@ -10,6 +10,10 @@
 // run of tokens; their k row ids and weights are staged in LDS, then the
 // 256 threads stream 16-byte vectors of every row (HBM bound: N*H reads,
 // T*H writes).  A row id >= N contributes NaN instead of being read.
+//
+// Without weights (a null pointer) every weight is 1, and the kernel is the
+// dispatch backward of section 12: each token's selected rows summed in slot
+// order (fmaf(1, v, acc) is the exact sum v + acc), rounded once.
 
 #include "device_common.h"
 #include "launch.h"
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int64_t t = t0 + q / k;
     if (t < T) {
       srow[q] = token_row[t0 * k + q];
-      sw[q] = to_f32<WD>(w[t0 * k + q]);
+      sw[q] = w ? to_f32<WD>(w[t0 * k + q]) : 1.0f;
     }
   }
   __syncthreads();

@@ -387,7 +387,68 @@ hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
                                           offsets, act, y, st);
 }
 
+// Plain grouped NT product on MFMA (bf16/f16, K and NB multiples of 8,
+// 16-byte aligned): the kernels launch_experts would pick for its down GEMM.
+template <int D>
+hipError_t launch_nt_mfma(const void* A, int64_t N, int64_t K, const void* B,
+                          int64_t NB, int E, const uint32_t* offsets, void* C,
+                          hipStream_t st) {
+  using S = typename Storage<D>::T;
+  const int nseg = E + 1;  // rows past offsets[E] are written as zeros
+  if (N < 96 * (int64_t)E) {
+    const uint32_t ncol = cdiv(NB, 128);
+    const uint32_t grid = tile_grid(ncol * (cdiv(N, 32) + (uint32_t)nseg));
+    hipLaunchKernelGGL((gemm_mfma_kernel<D, 32, 128, 1, false, MOE_DECODE_NT>),
+                       dim3(grid), dim3(256), 0, st, (const S*)A, (const S*)B,
+                       (const S*)B, (S*)C, offsets, N, (int)K, (int)NB, E,
+                       ncol, nseg);
+    return hipGetLastError();
+  }
+  const int64_t lim = (int64_t)1 << 31;
+  if (K * NB * 2 < lim && 256 * K * 2 < lim && 256 * NB * 2 < lim)
+    return launch_nt_big(A, D, N, (int)K, B, (int)NB, E, offsets, C, st);
+  const uint32_t ncol = cdiv(NB, 128);
+  const uint32_t grid = tile_grid(ncol * (cdiv(N, 128) + (uint32_t)nseg));
+  hipLaunchKernelGGL((gemm_mfma_kernel<D, 128, 128, 2, false, false>),
+                     dim3(grid), dim3(256), 0, st, (const S*)A, (const S*)B,
+                     (const S*)B, (S*)C, offsets, N, (int)K, (int)NB, E, ncol,
+                     nseg);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_nt_generic(const void* A, int64_t N, int64_t K,
+                             const void* B, int64_t NB, int E,
+                             const uint32_t* offsets, void* C,
+                             hipStream_t st) {
+  using S = typename Storage<D>::T;
+  const int nseg = E + 1;
+  const uint32_t ncol = cdiv(NB, 64);
+  const uint32_t grid = tile_grid(ncol * (cdiv(N, 64) + (uint32_t)nseg));
+  hipLaunchKernelGGL((gemm_generic_kernel<D, false>), dim3(grid), dim3(256),
+                     0, st, (const S*)A, (const S*)B, (const S*)B, (S*)C,
+                     offsets, N, (int)K, (int)NB, E, ncol, nseg);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_grouped_nt(const void* A, int dt, int64_t N, int64_t K,
+                             const void* B, int64_t NB, int E,
+                             const uint32_t* offsets, void* C,
+                             hipStream_t st) {
+  const uintptr_t al = (uintptr_t)A | (uintptr_t)B | (uintptr_t)C;
+  const bool mfma = dt != DT_F32 && K % 8 == 0 && NB % 8 == 0 && al % 16 == 0;
+  if (mfma && dt == DT_BF16)
+    return launch_nt_mfma<DT_BF16>(A, N, K, B, NB, E, offsets, C, st);
+  if (mfma)
+    return launch_nt_mfma<DT_F16>(A, N, K, B, NB, E, offsets, C, st);
+  switch (dt) {
+    case DT_F32: return launch_nt_generic<DT_F32>(A, N, K, B, NB, E, offsets, C, st);
+    case DT_F16: return launch_nt_generic<DT_F16>(A, N, K, B, NB, E, offsets, C, st);
+    default: return launch_nt_generic<DT_BF16>(A, N, K, B, NB, E, offsets, C, st);
+  }
+}
 
 hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
                           int64_t I, int E, const void* w_gate,

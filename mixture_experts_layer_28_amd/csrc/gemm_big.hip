@@ -295,6 +295,17 @@ hipError_t launch_pair(const void* xd, int64_t N, int64_t H, int64_t I,
 
 }  // namespace
 
+hipError_t launch_nt_big(const void* A, int dt, int64_t N, int K,
+                         const void* B, int NB, int E,
+                         const uint32_t* offsets, void* C, hipStream_t st) {
+  // segment E covers the rows past offsets[E]: they are written as zeros
+  if (dt == DT_BF16)
+    return launch_one<DT_BF16, false>(A, B, B, C, offsets, N, K, NB, E, E + 1,
+                                      st);
+  return launch_one<DT_F16, false>(A, B, B, C, offsets, N, K, NB, E, E + 1,
+                                   st);
+}
+
 hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
                               int64_t I, int E, const void* w_gate,
                               const void* w_up, const void* w_down,

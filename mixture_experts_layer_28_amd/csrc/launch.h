@@ -84,6 +84,47 @@ hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
                               const uint32_t* offsets, void* act, void* y,
                               hipStream_t st);
 
+// One plain grouped NT product C[r, :] = A[r, :] . B[e]^T for the rows r of
+// segment e (A [N,K], B [E,NB,K], C [N,NB], all of dtype dt); rows past
+// offsets[E] are written as zeros.  Picks the same kernels as
+// launch_experts.
+hipError_t launch_grouped_nt(const void* A, int dt, int64_t N, int64_t K,
+                             const void* B, int64_t NB, int E,
+                             const uint32_t* offsets, void* C, hipStream_t st);
+// The prefill-sized kernel of launch_experts_big for a plain product (bf16
+// or f16; the same size limits).
+hipError_t launch_nt_big(const void* A, int dt, int64_t N, int K,
+                         const void* B, int NB, int E,
+                         const uint32_t* offsets, void* C, hipStream_t st);
+
+// ---- training path ---------------------------------------------------------
+// Training forward: gate, up [N,I] (the raw products), act [N,I], y [N,H].
+hipError_t launch_experts_forward_training(
+    const void* xd, int dt, int64_t N, int64_t H, int64_t I, int E,
+    const void* w_gate, const void* w_up, const void* w_down,
+    const uint32_t* offsets, void* gate, void* up, void* act, void* y,
+    hipStream_t st);
+// Combine backward: dexp [N,H] (dtype dt), dw [T,k] FP32.
+hipError_t launch_combine_backward(const void* y, int dt, int64_t N,
+                                   int64_t T, int64_t H, int k,
+                                   const void* w, int wdt,
+                                   const uint32_t* token_row,
+                                   const void* dout, void* dexp, float* dw,
+                                   hipStream_t st);
+// Expert backward scratch: one transposed weight tensor, then dact, dg, du
+// [N,I] and the two input-gradient halves [N,H] (byte offsets, 256-aligned).
+struct ExpertsBackwardLayout {
+  size_t wt, dact, dg, du, dxg, dxu, total;
+};
+ExpertsBackwardLayout experts_backward_layout(int64_t N, int64_t H,
+                                              int64_t I, int64_t E, int dt);
+hipError_t launch_experts_backward(
+    const void* xd, int dt, int64_t N, int64_t H, int64_t I, int E,
+    const void* w_gate, const void* w_up, const void* w_down,
+    const uint32_t* offsets, const void* gate, const void* up,
+    const void* act, const void* dy, void* dxd, float* dwg, float* dwu,
+    float* dwd, void* workspace, hipStream_t st);
+
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(const void* y, int dt, int64_t N, int64_t T,
                           int64_t H, int k, const void* w, int wdt,

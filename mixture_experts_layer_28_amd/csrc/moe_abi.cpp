@@ -503,4 +503,99 @@ int moe_selected_router_backward(const void* logits, int ldt, int64_t T,
                     "moe_selected_router_backward");
 }
 
+int moe_experts_forward_training(const void* xd, int dt, int64_t N,
+                                 int64_t H, int64_t I, int64_t E,
+                                 const void* w_gate, const void* w_up,
+                                 const void* w_down, const uint32_t* offsets,
+                                 void* gate, void* up, void* act, void* y,
+                                 void* stream) {
+  const int s = check_experts(xd, dt, N, H, I, E, w_gate, w_up, w_down,
+                              offsets, act, y);
+  if (s != MOE_OK) return s;
+  if (N > 0 && (!gate || !up))
+    return fail(MOE_ERR_INVALID_ARG, "moe_experts_forward_training: null pointer");
+  if (N == 0) return ok();
+  return hip_status(moe::launch_experts_forward_training(
+                        xd, dt, N, H, I, (int)E, w_gate, w_up, w_down,
+                        offsets, gate, up, act, y, (hipStream_t)stream),
+                    "moe_experts_forward_training");
+}
+
+int moe_combine_backward(const void* y, int dt, int64_t N, int64_t T,
+                         int64_t H, int64_t top_k, const void* weights,
+                         int wdt, const uint32_t* token_row,
+                         const void* grad_out, void* grad_expert,
+                         float* grad_weights, void* stream) {
+  const int s = check_combine(y, dt, N, T, H, top_k, weights, wdt, token_row,
+                              grad_out);
+  if (s != MOE_OK) return s;
+  if (T > 0 && (!grad_expert || !grad_weights))
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine_backward: null pointer");
+  if (T == 0) return ok();
+  return hip_status(moe::launch_combine_backward(
+                        y, dt, N, T, H, (int)top_k, weights, wdt, token_row,
+                        grad_out, grad_expert, grad_weights,
+                        (hipStream_t)stream),
+                    "moe_combine_backward");
+}
+
+size_t moe_experts_backward_workspace_size(int64_t N, int64_t H, int64_t I,
+                                           int64_t E, int dt) {
+  if (!valid_dtype(dt) || N < 0 || N > kMaxRows || H < 1 || I < 1 || E < 1 ||
+      E > kMaxDispatchE || H > INT32_MAX || I > INT32_MAX)
+    return 0;
+  int64_t ei;
+  if (!mul_ok(E, I, &ei) || !bytes_ok(ei, H, 4) ||
+      !bytes_ok(N, H > I ? H : I, 16))
+    return 0;
+  return moe::experts_backward_layout(N, H, I, E, dt).total;
+}
+
+int moe_experts_backward(const void* xd, int dt, int64_t N, int64_t H,
+                         int64_t I, int64_t E, const void* w_gate,
+                         const void* w_up, const void* w_down,
+                         const uint32_t* offsets, const void* gate,
+                         const void* up, const void* act, const void* grad_y,
+                         void* grad_xd, float* grad_w_gate, float* grad_w_up,
+                         float* grad_w_down, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const char* f = "moe_experts_backward";
+  const int s = check_experts(xd, dt, N, H, I, E, w_gate, w_up, w_down,
+                              offsets, act, grad_y);
+  if (s != MOE_OK) return s;
+  if (!grad_w_gate || !grad_w_up || !grad_w_down || !offsets)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", f);
+  if (N > 0 && (!gate || !up || !grad_xd))
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", f);
+  const size_t need = moe_experts_backward_workspace_size(N, H, I, E, dt);
+  if (need == 0) return fail(MOE_ERR_SHAPE, "%s: sizes out of range", f);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace needs %zu bytes", f, need);
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", f);
+  // with no rows every weight gradient is zero, which the kernels write too
+  return hip_status(moe::launch_experts_backward(
+                        xd, dt, N, H, I, (int)E, w_gate, w_up, w_down,
+                        offsets, gate, up, act, grad_y, grad_xd, grad_w_gate,
+                        grad_w_up, grad_w_down, workspace,
+                        (hipStream_t)stream),
+                    f);
+}
+
+int moe_dispatch_backward(const void* grad_xd, int dt, int64_t N, int64_t T,
+                          int64_t H, int64_t top_k,
+                          const uint32_t* token_row, void* grad_x,
+                          void* stream) {
+  // the combine kernel with unit weights; FAKE weights pointer satisfies
+  // the shared check, the launch passes none
+  const int s = check_combine(grad_xd, dt, N, T, H, top_k, token_row, dt,
+                              token_row, grad_x);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  return hip_status(moe::launch_combine(grad_xd, dt, N, T, H, (int)top_k,
+                                        nullptr, MOE_F32, token_row, grad_x,
+                                        (hipStream_t)stream),
+                    "moe_dispatch_backward");
+}
+
 }  // extern "C"

@@ -312,8 +312,102 @@ def moe_selected_router_backward(logits, indices, grad_weights,
     return out
 
 
+def moe_experts_forward_training(xd, offsets, w_gate, w_up, w_down):
+    """Training forward over segments: returns dict gate, up, act [N,I]
+    (the cache the expert backward needs) and y [N,H]."""
+    xd, offsets = _c(xd), _c(offsets)
+    w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
+    dev = _dev(xd, offsets, w_gate, w_up, w_down)
+    N, H = xd.shape
+    E, I = _experts_weights(w_gate, w_up, w_down, H, xd.dtype)
+    _index(offsets, (E + 1,), "offsets")
+    out = {name: torch.empty((N, I), dtype=xd.dtype, device=dev)
+           for name in ("gate", "up", "act")}
+    out["y"] = torch.empty((N, H), dtype=xd.dtype, device=dev)
+    check(lib().moe_experts_forward_training(
+        _p(xd), _dt(xd, "xd"), N, H, I, E, _p(w_gate), _p(w_up), _p(w_down),
+        _p(offsets), _p(out["gate"]), _p(out["up"]), _p(out["act"]),
+        _p(out["y"]), _stream(dev)))
+    return out
+
+
+def moe_combine_backward(y, weights, token_row, grad_out):
+    """Gradients of moe_combine: (grad_expert [N,H] in y's dtype,
+    grad_weights [T,k] float32).  Rows no slot maps stay zero."""
+    y, weights = _c(y), _c(weights)
+    token_row, grad_out = _c(token_row), _c(grad_out)
+    dev = _dev(y, weights, token_row, grad_out)
+    N, H = y.shape
+    T, k = weights.shape
+    _index(token_row, (T, k), "token_row")
+    if grad_out.shape != (T, H) or grad_out.dtype != y.dtype:
+        raise ValueError("grad_out must be [T, H] in y's dtype")
+    grad_expert = torch.zeros((N, H), dtype=y.dtype, device=dev)
+    grad_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    check(lib().moe_combine_backward(
+        _p(y), _dt(y, "y"), N, T, H, k, _p(weights), _dt(weights, "weights"),
+        _p(token_row), _p(grad_out), _p(grad_expert), _p(grad_weights),
+        _stream(dev)))
+    return grad_expert, grad_weights
+
+
+def moe_experts_backward_workspace_size(N, H, I, E, dtype):
+    return lib().moe_experts_backward_workspace_size(N, H, I, E, _DT[dtype])
+
+
+def moe_experts_backward(xd, offsets, w_gate, w_up, w_down, cache, grad_y,
+                         workspace=None):
+    """Expert backward from the training cache (a dict with gate, up, act as
+    moe_experts_forward_training returns).  Returns dict grad_xd [N,H] and
+    float32 grad_w_gate, grad_w_up [E,I,H], grad_w_down [E,H,I]."""
+    xd, offsets, grad_y = _c(xd), _c(offsets), _c(grad_y)
+    w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
+    gate, up, act = _c(cache["gate"]), _c(cache["up"]), _c(cache["act"])
+    dev = _dev(xd, offsets, w_gate, w_up, w_down, gate, up, act, grad_y)
+    N, H = xd.shape
+    E, I = _experts_weights(w_gate, w_up, w_down, H, xd.dtype)
+    _index(offsets, (E + 1,), "offsets")
+    for name, t in (("gate", gate), ("up", up), ("act", act)):
+        if t.shape != (N, I) or t.dtype != xd.dtype:
+            raise ValueError("cache %s must be [N, I] in xd's dtype" % name)
+    if grad_y.shape != (N, H) or grad_y.dtype != xd.dtype:
+        raise ValueError("grad_y must be [N, H] in xd's dtype")
+    workspace, ws_bytes = _workspace(
+        workspace, moe_experts_backward_workspace_size(N, H, I, E, xd.dtype),
+        dev)
+    out = dict(grad_xd=torch.empty((N, H), dtype=xd.dtype, device=dev),
+               grad_w_gate=torch.empty((E, I, H), dtype=torch.float32,
+                                       device=dev),
+               grad_w_up=torch.empty((E, I, H), dtype=torch.float32,
+                                     device=dev),
+               grad_w_down=torch.empty((E, H, I), dtype=torch.float32,
+                                       device=dev))
+    check(lib().moe_experts_backward(
+        _p(xd), _dt(xd, "xd"), N, H, I, E, _p(w_gate), _p(w_up), _p(w_down),
+        _p(offsets), _p(gate), _p(up), _p(act), _p(grad_y),
+        _p(out["grad_xd"]), _p(out["grad_w_gate"]), _p(out["grad_w_up"]),
+        _p(out["grad_w_down"]), _p(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def moe_dispatch_backward(grad_xd, token_row, out=None):
+    """grad_x [T,H]: each token's selected rows of grad_xd [N,H] summed."""
+    grad_xd, token_row = _c(grad_xd), _c(token_row)
+    dev = _dev(grad_xd, token_row)
+    N, H = grad_xd.shape
+    T, k = token_row.shape
+    _index(token_row, (T, k), "token_row")
+    out = _out(out, (T, H), grad_xd.dtype, dev, "grad_x")
+    check(lib().moe_dispatch_backward(
+        _p(grad_xd), _dt(grad_xd, "grad_xd"), N, T, H, k, _p(token_row),
+        _p(out), _stream(dev)))
+    return out
+
+
 __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_experts_forward", "moe_combine", "moe_forward",
            "moe_forward_workspace_size", "moe_route_sigmoid_grouped",
            "moe_forward_sigmoid_grouped", "moe_selected_router_weights",
-           "moe_selected_router_backward", "_lib"]
+           "moe_selected_router_backward", "moe_experts_forward_training",
+           "moe_combine_backward", "moe_experts_backward_workspace_size",
+           "moe_experts_backward", "moe_dispatch_backward", "_lib"]

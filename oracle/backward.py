@@ -96,41 +96,62 @@ def swiglu_backward(g, u, da, fmt):
     return dg, du
 
 
+def _segments(offsets):
+    E = len(offsets) - 1
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if lo < hi:
+            yield e, lo, hi
+
+
+def down_backward(dy, act, offsets, w_down, fmt):
+    """The down projection's backward: dact [N,I] = dy . w_down[e] (rounded
+    to ``fmt``) and FP32 ddown [E,H,I] = dy_e^T . act_e."""
+    dy = decode(dy, fmt)
+    act = decode(act, fmt)
+    E = len(offsets) - 1
+    N, H = dy.shape
+    I = act.shape[1]
+    dact = np.zeros((N, I))
+    ddown = np.zeros((E, H, I))
+    for e, lo, hi in _segments(offsets):
+        wd = decode(np.asarray(w_down)[e], fmt)
+        dact[lo:hi] = round_to(dy[lo:hi] @ wd, fmt)
+        ddown[e] = dy[lo:hi].T @ act[lo:hi]
+    return dact, round_to(ddown, "f32")
+
+
+def proj_backward(dz, xd, offsets, w, fmt):
+    """The backward of z = xd . w[e]^T (gate or up): the input-gradient part
+    dz . w[e] [N,H] (rounded to ``fmt``) and FP32 dw [E,I,H] = dz_e^T . xd_e."""
+    dz = decode(dz, fmt)
+    xd = decode(xd, fmt)
+    E = len(offsets) - 1
+    N, I = dz.shape
+    H = xd.shape[1]
+    dx = np.zeros((N, H))
+    dw = np.zeros((E, I, H))
+    for e, lo, hi in _segments(offsets):
+        we = decode(np.asarray(w)[e], fmt)
+        dx[lo:hi] = round_to(dz[lo:hi] @ we, fmt)
+        dw[e] = dz[lo:hi].T @ xd[lo:hi]
+    return dx, round_to(dw, "f32")
+
+
 def experts_backward(xd, offsets, w_gate, w_up, w_down, cache, dy, fmt):
     """Expert backward from the training cache (gate, up, act) and the
     gradient dy [N,H] of the expert outputs.  Returns dict dinput [N,H]
     (values of ``fmt``) and FP32 dgate [E,I,H], dup [E,I,H], ddown [E,H,I],
-    following the experts page's order and rounding points (R-BPrec)."""
-    xd = decode(xd, fmt)
-    dy = decode(dy, fmt)
-    E = len(offsets) - 1
-    N, H = xd.shape
-    I = np.asarray(w_gate).shape[1]
-    dinput = np.zeros((N, H))
-    dgate = np.zeros((E, I, H))
-    dup = np.zeros((E, I, H))
-    ddown = np.zeros((E, H, I))
-    for e in range(E):
-        lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if lo == hi:
-            continue
-        wg = decode(np.asarray(w_gate)[e], fmt)
-        wu = decode(np.asarray(w_up)[e], fmt)
-        wd = decode(np.asarray(w_down)[e], fmt)
-        dye = dy[lo:hi]
-        # down projection backward: input gradient and weight gradient
-        da = round_to(dye @ wd, fmt)
-        ddown[e] = dye.T @ cache["act"][lo:hi]
-        dg, du = swiglu_backward(cache["gate"][lo:hi], cache["up"][lo:hi], da,
-                                 fmt)
-        # gate and up projection backwards, then their sum
-        dxg = round_to(dg @ wg, fmt)
-        dxu = round_to(du @ wu, fmt)
-        dgate[e] = dg.T @ xd[lo:hi]
-        dup[e] = du.T @ xd[lo:hi]
-        dinput[lo:hi] = round_to(dxg + dxu, fmt)
-    return {"dinput": dinput, "dgate": round_to(dgate, "f32"),
-            "dup": round_to(dup, "f32"), "ddown": round_to(ddown, "f32")}
+    plus the intermediates dact, dg, du [N,I] and dxg, dxu [N,H], following
+    the experts page's order and rounding points (R-BPrec)."""
+    dact, ddown = down_backward(dy, cache["act"], offsets, w_down, fmt)
+    dg, du = swiglu_backward(decode(cache["gate"], fmt),
+                             decode(cache["up"], fmt), dact, fmt)
+    dxg, dgate = proj_backward(dg, xd, offsets, w_gate, fmt)
+    dxu, dup = proj_backward(du, xd, offsets, w_up, fmt)
+    dinput = round_to(dxg + dxu, fmt)
+    return {"dinput": dinput, "dgate": dgate, "dup": dup, "ddown": ddown,
+            "dact": dact, "dg": dg, "du": du, "dxg": dxg, "dxu": dxu}
 
 
 def dispatch_backward(dinput, token_row, fmt):

@@ -277,3 +277,55 @@ def test_router_backward_rejects():
     a = list(args)
     a[2] = 0
     assert L.moe_selected_router_backward(*a) == 0
+
+
+def test_training_entry_points_reject():
+    L = _lib.lib()
+    # moe_experts_forward_training(xd, dt, N, H, I, E, wg, wu, wd, offsets,
+    #                              gate, up, act, y, stream)
+    base = [FAKE, 2, 100, 64, 32, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, None]
+    for i, v, st in [(1, 9, 3), (2, -1, 2), (5, 0, 2), (6, None, 1),
+                     (10, None, 1), (11, None, 1), (12, None, 1),
+                     (13, None, 1)]:
+        a = list(base)
+        a[i] = v
+        assert L.moe_experts_forward_training(*a) == st, (i, v)
+    # moe_combine_backward(y, dt, N, T, H, k, w, wdt, token_row, grad_out,
+    #                      grad_expert, grad_weights, stream)
+    base = [FAKE, 2, 20, 10, 16, 2, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None]
+    for i, v, st in [(1, 5, 3), (7, 5, 3), (5, 0, 1), (5, 8193, 4),
+                     (9, None, 1), (10, None, 1), (11, None, 1)]:
+        a = list(base)
+        a[i] = v
+        assert L.moe_combine_backward(*a) == st, (i, v)
+    # moe_dispatch_backward(grad_xd, dt, N, T, H, k, token_row, grad_x, stream)
+    base = [FAKE, 2, 20, 10, 16, 2, FAKE, FAKE, None]
+    for i, v, st in [(1, 5, 3), (5, 0, 1), (6, None, 1), (7, None, 1),
+                     (0, None, 1)]:
+        a = list(base)
+        a[i] = v
+        assert L.moe_dispatch_backward(*a) == st, (i, v)
+    a = list(base)
+    a[3] = 0
+    assert L.moe_dispatch_backward(*a) == 0
+
+
+def test_experts_backward_workspace_and_rejects():
+    L = _lib.lib()
+    N, H, I, E = 100, 64, 32, 4
+    ws = L.moe_experts_backward_workspace_size(N, H, I, E, 2)
+    # one transposed weight tensor, three [N,I] and two [N,H] buffers
+    assert ws >= (E * H * I + 3 * N * I + 2 * N * H) * 2 and ws % 256 == 0
+    assert L.moe_experts_backward_workspace_size(N, H, I, 0, 2) == 0
+    assert L.moe_experts_backward_workspace_size(N, H, I, E, 7) == 0
+    args = [FAKE, 2, N, H, I, E, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE, FAKE, FAKE, 0x10000, ws, None]
+    for i, v in [(19, ws - 1), (18, 0x10010), (18, None), (15, None),
+                 (17, None), (10, None), (14, None), (9, None)]:
+        a = list(args)
+        a[i] = v
+        assert L.moe_experts_backward(*a) == 1, (i, v)
+    a = list(args)
+    a[1] = 9
+    assert L.moe_experts_backward(*a) == 3
