@@ -72,6 +72,10 @@ def parse():
                         "moe_selected_router_weights and "
                         "moe_selected_router_backward alone at T = 2^16, "
                         "2^18, 2^20; one JSON line per case")
+    p.add_argument("--train", action="store_true",
+                   help="extension, not the benchmark: time one first-order "
+                        "training step (forward and the backward chain) of "
+                        "the workload; one JSON line")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU work: print the kernel statistics of a "
                         "rocprofv3 --kernel-trace --stats run as markdown")
@@ -325,6 +329,93 @@ def router_weights_sweep():
                       flush=True)
 
 
+TRAIN_STAGES = ["route", "router_weights", "dispatch", "experts_fwd",
+                "combine", "combine_bwd", "experts_bwd", "dispatch_bwd",
+                "router_bwd"]
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+
+
+def train_step_bench(args):
+    """Extension, not the benchmark: one first-order training step of the
+    MoE layer for a fixed output gradient -- softmax route, FP32 router
+    weights of the choice, dispatch, training forward, combine, then the
+    backward chain (combine, experts, dispatch, router).  Per-stage times
+    from torch events on the one stream every call is enqueued on."""
+    import torch
+
+    import mixture_experts_layer_28_amd as moe
+    from mixture_experts_layer_28_amd import workloads
+
+    dev = torch.device("cuda:0")
+    base, T = WORKLOADS[args.workload]
+    wl = workloads.make(base, T=T, device=dev)
+    T, H, I, E, k = wl["T"], wl["H"], wl["I"], wl["E"], wl["k"]
+    x, logits = wl["x"], wl["logits"]
+    wg, wu, wd = wl["w_gate"], wl["w_up"], wl["w_down"]
+    gen = torch.Generator(device=dev).manual_seed(5)
+    dout = torch.randn((T, H), generator=gen, device=dev).to(x.dtype)
+    N = T * k
+    ws = torch.empty(moe.moe_experts_backward_workspace_size(
+        N, H, I, E, x.dtype), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        mark(0)
+        idx, _ = moe.moe_route(logits, k, wl["renorm"])
+        mark(1)
+        w = moe.moe_selected_router_weights(logits, idx, "softmax",
+                                            wl["renorm"], index_type="u32")
+        mark(2)
+        d = moe.moe_dispatch(x, idx, E)
+        mark(3)
+        cache = moe.moe_experts_forward_training(d["xd"], d["offsets"], wg,
+                                                 wu, wd)
+        mark(4)
+        moe.moe_combine(cache["y"], w, d["token_row"])
+        mark(5)
+        dexp, dw = moe.moe_combine_backward(cache["y"], w, d["token_row"],
+                                            dout)
+        mark(6)
+        b = moe.moe_experts_backward(d["xd"], d["offsets"], wg, wu, wd, cache,
+                                     dexp, workspace=ws)
+        mark(7)
+        moe.moe_dispatch_backward(b["grad_xd"], d["token_row"])
+        mark(8)
+        moe.moe_selected_router_backward(logits, idx, dw, "softmax",
+                                         wl["renorm"], index_type="u32")
+        mark(9)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(10)]
+             for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(marks[i])
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    per = {name: sum(m[j].elapsed_time(m[j + 1]) for m in marks) / args.steps
+           for j, name in enumerate(TRAIN_STAGES)}
+    # 6 N H I FLOP forward (three products), 12 N H I backward (six)
+    flop = 18 * N * H * I
+    ms_step = elapsed / args.steps * 1e3
+    print(json.dumps({
+        "extension": "train_step", "metric": "MoE training step tokens/sec",
+        "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s",
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "tflops_per_step": round(flop / (ms_step * 1e-3) / 1e12, 1),
+        "config": {"workload": base, "T": T, "H": H, "I": I, "E": E,
+                   "top_k": k},
+        "stages_ms": {n: round(v, 4) for n, v in per.items()},
+        "experts_bwd_tflops": round(12 * N * H * I /
+                                    (per["experts_bwd"] * 1e-3) / 1e12, 1),
+        "experts_fwd_tflops": round(6 * N * H * I /
+                                    (per["experts_fwd"] * 1e-3) / 1e12, 1)}),
+        flush=True)
+
+
 def summarize_trace(trace_dir):
     """Markdown table of a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -418,6 +509,9 @@ def main():
         return
     if args.router_weights_sweep:
         router_weights_sweep()
+        return
+    if args.train:
+        train_step_bench(args)
         return
     if args.copy_calibration:
         copy_calibration()

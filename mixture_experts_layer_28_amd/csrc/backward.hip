@@ -19,8 +19,12 @@
 // The transposes cost one read and one write of a weight tensor each; the
 // NT kernels then run at their forward speed.  The weight gradients are
 // "TN" products over each expert's rows,
-//   ddown[e] = dy_e^T . act_e,  dgate[e] = dg_e^T . xd_e,  dup[e] = du_e^T . xd_e,
-// computed here by an LDS-tiled FP32 kernel (tn_kernel).  Elementwise
+//   ddown[e] = dy_e^T . act_e,  dgate[e] = dg_e^T . xd_e,  dup[e] = du_e^T . xd_e;
+// with bf16/f16 each operand's rows are first transposed expert by expert
+// into one contiguous [columns, rows of e] block (seg_transpose_kernel), so
+// the product is an NT GEMM whose K is the expert's row count, run by the
+// prefill GEMM kernel's weight-gradient form (gemm_big.hip); fp32 and
+// unaligned shapes use an LDS-tiled FP32 kernel (tn_kernel).  Elementwise
 // kernels do the SwiGLU forward and backward and the final add.
 
 #include "device_common.h"
@@ -60,6 +64,76 @@ __global__ __launch_bounds__(256) void transpose_kernel(
       if (r < R && c < C) dst[c * R + r] = tile[tx][i];
     }
     __syncthreads();
+  }
+}
+
+// ---- per-expert transpose: block e of out = in[lo:hi, :]^T ------------------
+// in [N, C]; expert e's rows [lo, hi) become the block at out + C*(lo + 8e)
+// laid out [C, Kp] with Kp = hi - lo rounded up to a multiple of 8, the
+// operand form of the weight-gradient GEMM: every row of the block starts
+// 16-byte aligned and its 16-byte chunks never cross into the next row.
+// Columns [hi - lo, Kp) are zeros (seg_pad_kernel).  Rows past offsets[E]
+// are not copied.  Tiles of 64 rows x 64 columns; each tile row's expert is
+// found by a binary search over offsets.
+__host__ __device__ inline int64_t pad8(int64_t n) { return (n + 7) & ~int64_t(7); }
+
+template <typename W>
+__global__ __launch_bounds__(256) void seg_transpose_kernel(
+    const W* __restrict__ in, W* __restrict__ out,
+    const uint32_t* __restrict__ offsets, int E, int64_t N, int64_t C) {
+  __shared__ W tile[64][65];
+  __shared__ int64_t rlo[64], rn[64], rbase[64];
+  int64_t nv = offsets[E];
+  nv = nv < N ? nv : N;
+  const int64_t nr = (nv + 63) / 64, nc = (C + 63) / 64;
+  const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+  for (int64_t b = blockIdx.x; b < nr * nc; b += gridDim.x) {
+    const int64_t rb = b / nc, cb = b % nc;
+    if (threadIdx.x < 64) {
+      const int64_t r = rb * 64 + tx;
+      int lo = 0, hi = E;  // largest e with offsets[e] <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if ((int64_t)offsets[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      const int64_t a = offsets[lo];
+      int64_t z = lo < E ? (int64_t)offsets[lo + 1] : a;
+      z = z < nv ? z : nv;
+      rlo[tx] = a;
+      rn[tx] = z - a;
+      rbase[tx] = C * (a + 8 * (int64_t)lo);
+    }
+    for (int i = ty; i < 64; i += 4) {
+      const int64_t r = rb * 64 + i, c = cb * 64 + tx;
+      if (r < nv && c < C) tile[i][tx] = in[r * C + c];
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+      const int64_t c = cb * 64 + i, r = rb * 64 + tx;
+      if (r < nv && c < C && r >= rlo[tx] && r - rlo[tx] < rn[tx])
+        out[rbase[tx] + c * pad8(rn[tx]) + (r - rlo[tx])] = tile[tx][i];
+    }
+    __syncthreads();
+  }
+}
+
+// Zeros in the padding columns [n, Kp) of every row of every expert's block.
+template <typename W>
+__global__ __launch_bounds__(256) void seg_pad_kernel(
+    W* __restrict__ out, const uint32_t* __restrict__ offsets, int E,
+    int64_t N, int64_t C) {
+  const int64_t total = (int64_t)E * C;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    const int e = (int)(q / C);
+    const int64_t c = q % C;
+    int64_t hi = offsets[e + 1];
+    hi = hi < N ? hi : N;
+    int64_t lo = offsets[e];
+    lo = lo < hi ? lo : hi;
+    const int64_t n = hi - lo, kp = pad8(n);
+    W* row = out + C * (lo + 8 * (int64_t)e) + c * kp;
+    for (int64_t k = n; k < kp; ++k) row[k] = W(0);
   }
 }
 
@@ -231,6 +305,21 @@ __global__ __launch_bounds__(256) void tn_kernel(
 }
 
 template <typename W>
+hipError_t seg_transpose(const void* in, void* out, const uint32_t* offsets,
+                         int E, int64_t N, int64_t C, hipStream_t st) {
+  const int64_t blocks = ((N + 63) / 64) * ((C + 63) / 64);
+  hipLaunchKernelGGL((seg_transpose_kernel<W>), dim3(capped(blocks)),
+                     dim3(256), 0, st, (const W*)in, (W*)out, offsets, E, N,
+                     C);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((seg_pad_kernel<W>),
+                     dim3(capped(((int64_t)E * C + 255) / 256)), dim3(256), 0,
+                     st, (W*)out, offsets, E, N, C);
+  return hipGetLastError();
+}
+
+template <typename W>
 hipError_t transpose(const void* in, void* out, int64_t E, int64_t R,
                      int64_t C, hipStream_t st) {
   const int64_t blocks = E * ((R + 63) / 64) * ((C + 63) / 64);
@@ -264,6 +353,26 @@ hipError_t tn_dt(const void* A, int dt, const void* B,
     case DT_F16: return tn<DT_F16>(A, B, offsets, N, E, M, NC, C, st);
     default: return tn<DT_BF16>(A, B, offsets, N, E, M, NC, C, st);
   }
+}
+
+// Weight gradient Cw[e] = A_e^T . B_e over each expert's rows (A [N,M],
+// B [N,NC] in dtype dt): on MFMA through per-expert transposed copies in
+// ta, tb when the shapes allow, else the FMA kernel.
+hipError_t wgrad(const void* A, int dt, const void* B,
+                 const uint32_t* offsets, int64_t N, int E, int64_t M,
+                 int64_t NC, float* Cw, void* ta, void* tb, hipStream_t st) {
+  const uintptr_t al = (uintptr_t)ta | (uintptr_t)tb | (uintptr_t)Cw;
+  const bool mfma = dt != DT_F32 && M % 8 == 0 && NC % 8 == 0 &&
+                    al % 16 == 0 && 640 * (N + 8) < ((int64_t)1 << 31) &&
+                    M <= INT32_MAX && NC <= INT32_MAX;
+  if (!mfma) return tn_dt(A, dt, B, offsets, N, E, M, NC, Cw, st);
+  hipError_t err = seg_transpose<uint16_t>(A, ta, offsets, E, N, M, st);
+  if (err == hipSuccess)
+    err = seg_transpose<uint16_t>(B, tb, offsets, E, N, NC, st);
+  if (err == hipSuccess)
+    err = launch_wgrad_big(ta, dt, N, (int)M, tb, (int)NC, E, offsets, Cw,
+                           st);
+  return err;
 }
 
 template <int D>
@@ -379,6 +488,9 @@ ExpertsBackwardLayout experts_backward_layout(int64_t N, int64_t H,
   L.du = take((size_t)N * I * s);
   L.dxg = take((size_t)N * H * s);
   L.dxu = take((size_t)N * H * s);
+  // per-expert transposed copies: N rows plus 8 padding rows per expert
+  L.ta = take((size_t)(N + 8 * E) * (H > I ? H : I) * s);
+  L.tb = take((size_t)(N + 8 * E) * (H > I ? H : I) * s);
   L.total = at;
   return L;
 }
@@ -397,12 +509,14 @@ hipError_t launch_experts_backward(
   void* du = ws + L.du;
   void* dxg = ws + L.dxg;
   void* dxu = ws + L.dxu;
+  void* ta = ws + L.ta;
+  void* tb = ws + L.tb;
   // down projection: input gradient through Wd^T [E,I,H], weight gradient
   hipError_t err = transpose_dt(w_down, dt, wt, E, H, I, st);
   if (err == hipSuccess)
     err = launch_grouped_nt(dy, dt, N, H, wt, I, E, offsets, dact, st);
   if (err == hipSuccess)
-    err = tn_dt(dy, dt, act, offsets, N, E, H, I, dwd, st);
+    err = wgrad(dy, dt, act, offsets, N, E, H, I, dwd, ta, tb, st);
   // SwiGLU backward
   if (err == hipSuccess)
     err = MOE_BY_DT(dt, elementwise_bwd, gate, up, dact, dg, du, N * I, st);
@@ -417,9 +531,9 @@ hipError_t launch_experts_backward(
   if (err == hipSuccess)
     err = MOE_BY_DT(dt, elementwise_add, dxg, dxu, dxd, N * H, st);
   if (err == hipSuccess)
-    err = tn_dt(dg, dt, xd, offsets, N, E, I, H, dwg, st);
+    err = wgrad(dg, dt, xd, offsets, N, E, I, H, dwg, ta, tb, st);
   if (err == hipSuccess)
-    err = tn_dt(du, dt, xd, offsets, N, E, I, H, dwu, st);
+    err = wgrad(du, dt, xd, offsets, N, E, I, H, dwu, ta, tb, st);
   return err;
 }
 

@@ -41,14 +41,23 @@ constexpr int kFM = kBM / 4 / 16;                 // MFMA row tiles per wave, at
 constexpr int kStage = (kBM + kBN) * kBK;         // elements of one LDS stage
 constexpr size_t kLds = 2 * kStage * 2;           // two stages of 16-bit data
 
-template <int D, bool GATEUP>
+// WG: the weight-gradient form.  Per expert e with rows [lo, hi) of a
+// dispatch, Cw[e] [M, NB] (FP32) = A_e . B_e^T with A_e = A + (lo + 8e) * M
+// holding [M, Kp] and B_e = B0 + (lo + 8e) * NB holding [NB, Kp], Kp =
+// hi - lo rounded up to a multiple of 8 with zeros past hi - lo (each
+// expert's rows transposed into one block whose rows are 16-byte aligned),
+// so K = Kp varies per expert.  The tiles are E x ceil(M / kBM) x ncol
+// (balanced row blocks), dealt to the XCDs in contiguous ranges; an expert
+// without rows writes zeros.  N is the row count of the dispatch, M passes
+// in `K`.
+template <int D, bool GATEUP, bool WG = false>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const typename Storage<D>::T* __restrict__ A,
     const typename Storage<D>::T* __restrict__ B0,
     const typename Storage<D>::T* __restrict__ B1,
     typename Storage<D>::T* __restrict__ C,
     const uint32_t* __restrict__ offsets, int64_t N, int K, int NB, int E,
-    uint32_t ncol, int nseg) {
+    uint32_t ncol, int nseg, float* __restrict__ Cw = nullptr) {
   using S = typename Storage<D>::T;
   using V = typename Frag<D>::V;
   constexpr int WN = 2, NT = 512;
@@ -65,18 +74,58 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   __shared__ TileInfo ti;
 
   const int tid = threadIdx.x;
-  if (tid < 64)
-    locate_tile(blockIdx.x, gridDim.x, offsets, E, N, kBM, ncol, nseg, &ti,
-                true);
-  __syncthreads();
-  if (!ti.found) return;
-  const int e = uniform(ti.e);
-  const int64_t row0 = uniform(ti.row0);
-  const int arows = uniform(ti.rows);             // 1 .. kBM
+  const int64_t Mw = K;  // the weight-gradient form's M (rows of Cw[e])
+  int e, arows;
+  int64_t row0, n0;
+  const S* Ab = A;
+  const S* Bb = B0;
+  if constexpr (WG) {
+    // static map: tile L -> (expert, row block, column block)
+    const int64_t M = K;
+    const uint32_t nmb = (uint32_t)((M + kBM - 1) / kBM);
+    const uint32_t total = (uint32_t)E * nmb * ncol;
+    const uint32_t per = (total + 7u) / 8u, local = blockIdx.x / 8u;
+    const uint32_t L = (blockIdx.x % 8u) * per + local;
+    if (local >= per || L >= total) return;
+    e = (int)(L / (nmb * ncol));
+    const uint32_t l = L % (nmb * ncol);
+    const uint32_t grp = l / (8u * ncol), first = grp * 8u;
+    const uint32_t gs = nmb - first < 8u ? nmb - first : 8u;
+    const uint32_t rem = l - grp * 8u * ncol;
+    const int64_t mb = first + rem % gs;
+    n0 = (int64_t)(rem / gs) * TCOLS;
+    const int64_t a = mb * M / nmb, z = (mb + 1) * M / nmb;
+    row0 = a;
+    arows = (int)(z - a);
+    int64_t hi = uniform((int64_t)offsets[e + 1]);
+    hi = hi < N ? hi : N;
+    int64_t lo = uniform((int64_t)offsets[e]);
+    lo = lo < hi ? lo : hi;
+    K = (int)(((hi - lo) + 7) & ~int64_t(7));
+    Ab = A + (lo + 8 * (int64_t)e) * M;
+    Bb = B0 + (lo + 8 * (int64_t)e) * (int64_t)NB;
+    if (K == 0) {  // no rows: a zero gradient
+      float* ce = Cw + (int64_t)e * M * NB;
+      for (int q = tid; q < kBM * TCOLS; q += NT) {
+        const int64_t r = row0 + q / TCOLS, c = n0 + q % TCOLS;
+        if (r < row0 + arows && c < NB) ce[r * NB + c] = 0.0f;
+      }
+      return;
+    }
+  } else {
+    if (tid < 64)
+      locate_tile(blockIdx.x, gridDim.x, offsets, E, N, kBM, ncol, nseg, &ti,
+                  true);
+    __syncthreads();
+    if (!ti.found) return;
+    e = uniform(ti.e);
+    row0 = uniform(ti.row0);
+    arows = uniform(ti.rows);                     // 1 .. kBM
+    n0 = (int64_t)uniform(ti.col) * TCOLS;
+  }
   const int64_t tend = row0 + arows;
-  const int64_t n0 = (int64_t)uniform(ti.col) * TCOLS;
 
-  if (e >= E) {  // rows of out-of-range experts: zeros
+  if (!WG && e >= E) {  // rows of out-of-range experts: zeros
     for (int q = tid; q < kBM * TCOLS; q += NT) {
       const int64_t r = row0 + q / TCOLS, c = n0 + q % TCOLS;
       if (r < tend && c < NB) C[r * NB + c] = from_f32<D>(0.0f);
@@ -86,14 +135,18 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 
   const uint32_t rowbytes = (uint32_t)K * sizeof(S);
   // the A resource spans this tile's rows only, so every range fits in
-  // 31 bits and OOB (2^31) is always past the end
+  // 31 bits and OOB (2^31) is always past the end; in the weight-gradient
+  // form B's resource spans the tile's columns only, too
   const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(A + row0 * K, (uint64_t)arows * rowbytes);
-  const uint64_t wbytes = (uint64_t)NB * rowbytes;
+      make_rsrc(Ab + row0 * K, (uint64_t)arows * rowbytes);
+  const int64_t bcols = NB - n0 < kBN ? NB - n0 : kBN;
   const __amdgpu_buffer_rsrc_t rB0 =
-      make_rsrc(B0 + (int64_t)e * NB * K, wbytes);
+      WG ? make_rsrc(Bb + n0 * K, (uint64_t)bcols * rowbytes)
+         : make_rsrc(B0 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes);
   const __amdgpu_buffer_rsrc_t rB1 =
-      GATEUP ? make_rsrc(B1 + (int64_t)e * NB * K, wbytes) : rB0;
+      GATEUP ? make_rsrc(B1 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes)
+             : rB0;
+  const int64_t boff = WG ? 0 : n0;  // B row of the tile's first column
   constexpr uint32_t OOB = 0x80000000u;
 
   const int wid = uniform(tid >> 6), lane = tid & 63;
@@ -126,7 +179,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         const bool up = GATEUP && (b - ABLK) * 8 >= kBN / 2;  // uniform
         const int br = up ? r - kBN / 2 : r;
         buffer_load_lds16(up ? rB1 : rB0, base + b * 512,
-                          kin ? (uint32_t)(n0 + br) * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
+                          kin ? (uint32_t)(boff + br) * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
       }
     }
   };
@@ -225,6 +278,16 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       for (int q = 0; q < 4; ++q) {
         const int64_t r = row0 + tr0 + i * 16 + (lane >> 4) * 4 + q;
         if (r >= tend) continue;
+        if constexpr (WG) {
+          // M arrives as the kernel's K argument; K is now the expert's rows
+          float* cw = Cw + ((int64_t)e * Mw + r) * NB;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t c = n0 + wn * TN + j * 16 + (lane & 15);
+            if (c < NB) cw[c] = acc[i][j][q];
+          }
+          continue;
+        }
         S* crow = C + r * NB;
         if (GATEUP) {
           constexpr int H2 = FN / 2;
@@ -294,6 +357,45 @@ hipError_t launch_pair(const void* xd, int64_t N, int64_t H, int64_t I,
 }
 
 }  // namespace
+
+hipError_t launch_wgrad_big(const void* A, int dt, int64_t N, int M,
+                            const void* B, int NC, int E,
+                            const uint32_t* offsets, float* Cw,
+                            hipStream_t st) {
+  const uint32_t ncol = cdiv(NC, kBN);
+  const uint32_t nmb = cdiv(M, kBM);
+  const uint32_t grid = tile_grid((uint32_t)E * nmb * ncol);
+  if (dt == DT_BF16) {
+    using S = typename Storage<DT_BF16>::T;
+    static bool attr = false;
+    if (!attr) {
+      hipError_t err = hipFuncSetAttribute(
+          (const void*)gemm_big_kernel<DT_BF16, false, true>,
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+      if (err != hipSuccess) return err;
+      attr = true;
+    }
+    hipLaunchKernelGGL((gemm_big_kernel<DT_BF16, false, true>), dim3(grid),
+                       dim3(512), kLds, st, (const S*)A, (const S*)B,
+                       (const S*)B, (S*)nullptr, offsets, N, M, NC, E, ncol, 0,
+                       Cw);
+  } else {
+    using S = typename Storage<DT_F16>::T;
+    static bool attr = false;
+    if (!attr) {
+      hipError_t err = hipFuncSetAttribute(
+          (const void*)gemm_big_kernel<DT_F16, false, true>,
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+      if (err != hipSuccess) return err;
+      attr = true;
+    }
+    hipLaunchKernelGGL((gemm_big_kernel<DT_F16, false, true>), dim3(grid),
+                       dim3(512), kLds, st, (const S*)A, (const S*)B,
+                       (const S*)B, (S*)nullptr, offsets, N, M, NC, E, ncol, 0,
+                       Cw);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_nt_big(const void* A, int dt, int64_t N, int K,
                          const void* B, int NB, int E,

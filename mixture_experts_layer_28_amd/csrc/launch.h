@@ -112,9 +112,10 @@ hipError_t launch_combine_backward(const void* y, int dt, int64_t N,
                                    const void* dout, void* dexp, float* dw,
                                    hipStream_t st);
 // Expert backward scratch: one transposed weight tensor, then dact, dg, du
-// [N,I] and the two input-gradient halves [N,H] (byte offsets, 256-aligned).
+// [N,I], the two input-gradient halves [N,H], and two per-expert transposed
+// operand copies of N * max(H, I) elements (byte offsets, 256-aligned).
 struct ExpertsBackwardLayout {
-  size_t wt, dact, dg, du, dxg, dxu, total;
+  size_t wt, dact, dg, du, dxg, dxu, ta, tb, total;
 };
 ExpertsBackwardLayout experts_backward_layout(int64_t N, int64_t H,
                                               int64_t I, int64_t E, int dt);
@@ -124,6 +125,16 @@ hipError_t launch_experts_backward(
     const uint32_t* offsets, const void* gate, const void* up,
     const void* act, const void* dy, void* dxd, float* dwg, float* dwu,
     float* dwd, void* workspace, hipStream_t st);
+
+// Weight gradients on MFMA: Cw[e] [M, NC] FP32 = A_e . B_e^T where A_e
+// (A + (lo + 8e)*M) is [M, Kp] and B_e (B + (lo + 8e)*NC) is [NC, Kp] for
+// the rows [lo, lo + n_e) of expert e, Kp = n_e rounded up to a multiple of
+// 8 with zero padding (each expert's rows transposed into one block).
+// bf16/f16; M, NC multiples of 8; 16-byte aligned; 640 * (N + 8) < 2^31.
+hipError_t launch_wgrad_big(const void* A, int dt, int64_t N, int M,
+                            const void* B, int NC, int E,
+                            const uint32_t* offsets, float* Cw,
+                            hipStream_t st);
 
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(const void* y, int dt, int64_t N, int64_t T,
