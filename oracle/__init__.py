@@ -25,6 +25,9 @@ Parity status of each function (what pins it is listed in the test files
                               brute-force loops)
 * ``moe.combine``             pinned (k=1 identity, brute force)
 * ``moe.forward``             pinned (brute force at T<=4, identical experts)
+* ``moe.clipped_silu_times`` and ``experts(..., clip=...)``
+                              pinned (reduces to the plain SwiGLU, torch
+                              clamp/sigmoid, closed forms at the clamps)
 * ``grouped.route_sigmoid_grouped``  pinned (golden cases, brute force by
                               counting, sort reduction, scipy ``expit``)
 * ``grouped.forward_sigmoid_grouped`` pinned (per-token sum, identical

@@ -34,6 +34,13 @@ its reason in the design notes of the repository):
           products themselves are exact sums (float64) rounded once.
 * R-SwiGLU act = SiLU(gate) * up, SiLU(g) = g / (1 + exp(-g)); no clamp and
           no alpha.
+* R-Clip  the clipped variant (MindSpeed-Ops page, ``clipped_swiglu``
+          parameter table: swiglu_alpha, default 1.702, and swiglu_limit L
+          >= 0, default 7, with the gate clamped from above at L and up to
+          [-L, L]; the page shows no formula): act = gc * sigmoid(alpha * gc)
+          * uc with gc = min(gate, L), uc = min(max(up, -L), L), the plain
+          swish-with-parameter reading of "SwiGLU's alpha".  NaN propagates
+          through the clamps.
 * R-Comb  combine sums w[t,j] * y[t,j] over the k slots and rounds once to
           the activation dtype; the routing weights are applied here only.
 """
@@ -157,7 +164,19 @@ def silu_times(g, u):
         return g * u / (1.0 + np.exp(-g))
 
 
-def expert_rows(xd, e, w_gate, w_up, w_down, fmt):
+def clipped_silu_times(g, u, alpha, limit):
+    """R-Clip, the clipped SwiGLU of the MindSpeed-Ops page (``clipped_swiglu``
+    parameter table): the gate is clamped from above at ``limit``, the up
+    value to [-limit, limit], and the activation is the swish with parameter
+    ``alpha`` of the clamped gate times the clamped up value:
+    gc * u_c / (1 + exp(-alpha * gc)), float64, NaN propagating."""
+    gc = np.minimum(g, limit)
+    uc = np.minimum(np.maximum(u, -limit), limit)
+    with np.errstate(over="ignore"):
+        return gc * uc / (1.0 + np.exp(-alpha * gc))
+
+
+def expert_rows(xd, e, w_gate, w_up, w_down, fmt, clip=None):
     """One expert applied to rows ``xd`` [n,H] (float64 values of ``fmt``).
 
     gate/up: [I,H] slices of the [E,I,H] weights; down: [H,I] slice of the
@@ -167,16 +186,18 @@ def expert_rows(xd, e, w_gate, w_up, w_down, fmt):
     """
     g = round_to(xd @ w_gate.T, fmt)
     u = round_to(xd @ w_up.T, fmt)
-    a = round_to(silu_times(g, u), fmt)
+    a = round_to(silu_times(g, u) if clip is None
+                 else clipped_silu_times(g, u, *clip), fmt)
     return round_to(a @ w_down.T, fmt)
 
 
-def experts(xd, offsets, w_gate, w_up, w_down, fmt, rows=None):
+def experts(xd, offsets, w_gate, w_up, w_down, fmt, rows=None, clip=None):
     """Grouped SwiGLU over expert segments.
 
     xd [N,H], offsets [E+1]; weights in ``fmt`` (decoded here).  If ``rows``
     is given, only those dispatched rows are computed (returned in that
-    order); otherwise all N rows.
+    order); otherwise all N rows.  ``clip`` = (alpha, limit) selects the
+    clipped SwiGLU activation.
     """
     xd = decode(xd, fmt)
     E = len(offsets) - 1
@@ -193,7 +214,7 @@ def experts(xd, offsets, w_gate, w_up, w_down, fmt, rows=None):
         wu = decode(np.asarray(w_up)[e], fmt)
         wd = decode(np.asarray(w_down)[e], fmt)
         assert wg.shape == (I, H) and wd.shape == (H, I)
-        out[sel] = expert_rows(xd[want[sel]], e, wg, wu, wd, fmt)
+        out[sel] = expert_rows(xd[want[sel]], e, wg, wu, wd, fmt, clip)
     return out
 
 
