@@ -152,6 +152,22 @@ int moe_experts_forward(const void* xd, int dt, int64_t N, int64_t H,
                         void* stream);
 
 /*
+ * moe_experts_forward_clipped - moe_experts_forward with the clipped SwiGLU
+ * activation (MindSpeed-Ops page, clipped_swiglu: swiglu_alpha, default
+ * 1.702, and swiglu_limit, default 7).  Arguments as moe_experts_forward
+ * plus alpha (finite) and limit (finite, >= 0); act becomes
+ *   gc * sigmoid(alpha * gc) * uc,  gc = min(g, limit),
+ *   uc = min(max(u, -limit), limit)
+ * in FP32 from the rounded g and u, rounded to dt (NaN stays NaN through
+ * the clamps).  Violations: MOE_ERR_INVALID_ARG.
+ */
+int moe_experts_forward_clipped(const void* xd, int dt, int64_t N, int64_t H,
+                                int64_t I, int64_t E, const void* w_gate,
+                                const void* w_up, const void* w_down,
+                                const uint32_t* offsets, float alpha,
+                                float limit, void* act, void* y, void* stream);
+
+/*
  * moe_combine - weighted merge back into token order (guide, section 6).
  *
  *   y         [N,H]      dt      expert output rows

@@ -11,7 +11,8 @@ only marshal arguments.
 from .ops import (moe_combine, moe_combine_backward, moe_dispatch,
                   moe_dispatch_backward, moe_dispatch_workspace_size,
                   moe_experts_backward, moe_experts_backward_workspace_size,
-                  moe_experts_forward, moe_experts_forward_training,
+                  moe_experts_forward, moe_experts_forward_clipped,
+                  moe_experts_forward_training,
                   moe_forward, moe_forward_sigmoid_grouped,
                   moe_forward_workspace_size, moe_route,
                   moe_route_sigmoid_grouped, moe_selected_router_backward,
@@ -23,4 +24,5 @@ __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_forward_sigmoid_grouped", "moe_selected_router_weights",
            "moe_selected_router_backward", "moe_experts_forward_training",
            "moe_combine_backward", "moe_experts_backward_workspace_size",
-           "moe_experts_backward", "moe_dispatch_backward"]
+           "moe_experts_backward", "moe_dispatch_backward",
+           "moe_experts_forward_clipped"]

@@ -29,6 +29,9 @@ SIGNATURES = {
                             _P, _P, _P, _P, _SZ, _P]),
     "moe_experts_forward": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P,
                                    _P, _P, _P, _P, _P]),
+    "moe_experts_forward_clipped": (_INT, [_P, _INT, _I64, _I64, _I64, _I64,
+                                           _P, _P, _P, _P, _F32, _F32, _P, _P,
+                                           _P]),
     "moe_combine": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P,
                            _P, _P]),
     "moe_forward_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I64, _INT,

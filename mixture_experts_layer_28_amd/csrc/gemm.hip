@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const typename Storage<D>::T* __restrict__ B1,
     typename Storage<D>::T* __restrict__ C,
     const uint32_t* __restrict__ offsets, int64_t N, int K, int NB, int E,
-    uint32_t ncol, int nseg) {
+    uint32_t ncol, int nseg, Swiglu sw = Swiglu{}) {
   using S = typename Storage<D>::T;
   using V = typename Frag<D>::V;
   constexpr int BK = 64;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
           if (c < NB) {
             const float g = to_f32<D>(from_f32<D>(acc[i][j][q]));
             const float u = to_f32<D>(from_f32<D>(acc[i][j + H2][q]));
-            crow[c] = from_f32<D>(silu_mul(g, u));
+            crow[c] = from_f32<D>(swiglu_act(g, u, sw));
           }
         }
       } else {
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
     const typename Storage<D>::T* __restrict__ B1,
     typename Storage<D>::T* __restrict__ C,
     const uint32_t* __restrict__ offsets, int64_t N, int K, int NB, int E,
-    uint32_t ncol, int nseg) {
+    uint32_t ncol, int nseg, Swiglu sw = Swiglu{}) {
   constexpr int BM = 64, BN = 64, BK = 16;
   constexpr int TCOLS = GATEUP ? 32 : 64;
   __shared__ float As[BK][BM + 1];
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
         if (c < NB) {
           const float g = to_f32<D>(from_f32<D>(acc[i][j]));
           const float u = to_f32<D>(from_f32<D>(acc[i][j + 2]));
-          C[r * NB + c] = from_f32<D>(silu_mul(g, u));
+          C[r * NB + c] = from_f32<D>(swiglu_act(g, u, sw));
         }
       }
     } else {
@@ -321,7 +321,7 @@ template <int D, int BM, int BN, int WGM, bool NTW>
 hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                             int E, const void* wg, const void* wu,
                             const void* wd, const uint32_t* offsets,
-                            void* act, void* y, hipStream_t st) {
+                            void* act, void* y, hipStream_t st, Swiglu sw) {
   using S = typename Storage<D>::T;
   {
     const uint32_t ncol = cdiv(I, BN / 2);
@@ -329,7 +329,7 @@ hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
     hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, true, NTW>), dim3(grid),
                        dim3(256), 0, st, (const S*)xd, (const S*)wg,
                        (const S*)wu, (S*)act, offsets, N, (int)H, (int)I, E,
-                       ncol, E);
+                       ncol, E, sw);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -348,14 +348,14 @@ hipError_t launch_generic_pair(const void* xd, int64_t N, int64_t H,
                                int64_t I, int E, const void* wg,
                                const void* wu, const void* wd,
                                const uint32_t* offsets, void* act, void* y,
-                               hipStream_t st) {
+                               hipStream_t st, Swiglu sw) {
   using S = typename Storage<D>::T;
   {
     const uint32_t ncol = cdiv(I, 32);
     const uint32_t grid = tile_grid(ncol * (cdiv(N, 64) + (uint32_t)E));
     hipLaunchKernelGGL((gemm_generic_kernel<D, true>), dim3(grid), dim3(256),
                        0, st, (const S*)xd, (const S*)wg, (const S*)wu,
-                       (S*)act, offsets, N, (int)H, (int)I, E, ncol, E);
+                       (S*)act, offsets, N, (int)H, (int)I, E, ncol, E, sw);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -372,19 +372,19 @@ template <int D>
 hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
                           int E, const void* wg, const void* wu,
                           const void* wd, const uint32_t* offsets, void* act,
-                          void* y, hipStream_t st) {
+                          void* y, hipStream_t st, Swiglu sw) {
   // Few rows per expert (decode): short row blocks waste less work.
   if (N < 96 * (int64_t)E)
     return launch_mfma_pair<D, 32, 128, 1, MOE_DECODE_NT>(xd, N, H, I, E, wg, wu, wd,
-                                           offsets, act, y, st);
+                                           offsets, act, y, st, sw);
   // Prefill: 256 x 256 tiles when every buffer range fits 31 bits.
   const int64_t lim = (int64_t)1 << 31;
   if (H * I * 2 < lim && 256 * H * 2 < lim && 256 * I * 2 < lim) {
     return launch_experts_big(xd, D, N, H, I, E, wg, wu, wd, offsets, act, y,
-                              st);
+                              st, sw);
   }
   return launch_mfma_pair<D, 128, 128, 2, false>(xd, N, H, I, E, wg, wu, wd,
-                                          offsets, act, y, st);
+                                          offsets, act, y, st, sw);
 }
 
 // Plain grouped NT product on MFMA (bf16/f16, K and NB multiples of 8,
@@ -454,27 +454,27 @@ hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
                           int64_t I, int E, const void* w_gate,
                           const void* w_up, const void* w_down,
                           const uint32_t* offsets, void* act, void* y,
-                          hipStream_t st) {
+                          hipStream_t st, Swiglu sw) {
   const uintptr_t al = (uintptr_t)xd | (uintptr_t)w_gate | (uintptr_t)w_up |
                        (uintptr_t)w_down | (uintptr_t)act | (uintptr_t)y;
   const bool mfma = dt != DT_F32 && H % 8 == 0 && I % 8 == 0 && al % 16 == 0;
   if (mfma) {
     if (dt == DT_BF16)
       return launch_mfma_dt<DT_BF16>(xd, N, H, I, E, w_gate, w_up, w_down,
-                                     offsets, act, y, st);
+                                     offsets, act, y, st, sw);
     return launch_mfma_dt<DT_F16>(xd, N, H, I, E, w_gate, w_up, w_down,
-                                  offsets, act, y, st);
+                                  offsets, act, y, st, sw);
   }
   switch (dt) {
     case DT_F32:
       return launch_generic_pair<DT_F32>(xd, N, H, I, E, w_gate, w_up, w_down,
-                                         offsets, act, y, st);
+                                         offsets, act, y, st, sw);
     case DT_F16:
       return launch_generic_pair<DT_F16>(xd, N, H, I, E, w_gate, w_up, w_down,
-                                         offsets, act, y, st);
+                                         offsets, act, y, st, sw);
     default:
       return launch_generic_pair<DT_BF16>(xd, N, H, I, E, w_gate, w_up,
-                                          w_down, offsets, act, y, st);
+                                          w_down, offsets, act, y, st, sw);
   }
 }
 

@@ -57,7 +57,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const typename Storage<D>::T* __restrict__ B1,
     typename Storage<D>::T* __restrict__ C,
     const uint32_t* __restrict__ offsets, int64_t N, int K, int NB, int E,
-    uint32_t ncol, int nseg, float* __restrict__ Cw = nullptr) {
+    uint32_t ncol, int nseg, float* __restrict__ Cw = nullptr,
+    Swiglu sw = Swiglu{}) {
   using S = typename Storage<D>::T;
   using V = typename Frag<D>::V;
   constexpr int WN = 2, NT = 512;
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
             if (c < NB) {
               const float g = to_f32<D>(from_f32<D>(acc[i][j][q]));
               const float u = to_f32<D>(from_f32<D>(acc[i][j + H2][q]));
-              crow[c] = from_f32<D>(silu_mul(g, u));
+              crow[c] = from_f32<D>(swiglu_act(g, u, sw));
             }
           }
         } else {
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 template <int D, bool GATEUP>
 hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
                       const uint32_t* offsets, int64_t N, int K, int NB,
-                      int E, int nseg, hipStream_t st) {
+                      int E, int nseg, hipStream_t st, Swiglu sw = Swiglu{}) {
   using S = typename Storage<D>::T;
   static bool attr = false;
   if (!attr) {
@@ -339,7 +340,7 @@ hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
   const uint32_t grid = tile_grid(ncol * (cdiv(N, kBM) + (uint32_t)nseg));
   hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP>), dim3(grid), dim3(512),
                      kLds, st, (const S*)A, (const S*)B0, (const S*)B1, (S*)C,
-                     offsets, N, K, NB, E, ncol, nseg);
+                     offsets, N, K, NB, E, ncol, nseg, nullptr, sw);
   return hipGetLastError();
 }
 
@@ -347,9 +348,9 @@ template <int D>
 hipError_t launch_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                        int E, const void* wg, const void* wu, const void* wd,
                        const uint32_t* offsets, void* act, void* y,
-                       hipStream_t st) {
+                       hipStream_t st, Swiglu sw) {
   hipError_t err = launch_one<D, true>(xd, wg, wu, act, offsets, N, (int)H,
-                                       (int)I, E, E, st);
+                                       (int)I, E, E, st, sw);
   if (err != hipSuccess) return err;
   timing_mark(5, st);
   return launch_one<D, false>(act, wd, wd, y, offsets, N, (int)I, (int)H, E,
@@ -412,12 +413,12 @@ hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
                               int64_t I, int E, const void* w_gate,
                               const void* w_up, const void* w_down,
                               const uint32_t* offsets, void* act, void* y,
-                              hipStream_t st) {
+                              hipStream_t st, Swiglu sw) {
   if (dt == DT_BF16)
     return launch_pair<DT_BF16>(xd, N, H, I, E, w_gate, w_up, w_down, offsets,
-                                act, y, st);
+                                act, y, st, sw);
   return launch_pair<DT_F16>(xd, N, H, I, E, w_gate, w_up, w_down, offsets,
-                             act, y, st);
+                             act, y, st, sw);
 }
 
 }  // namespace moe

@@ -134,6 +134,16 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
+// The gate+up epilogue's activation (Swiglu in launch.h).  The clamps keep
+// a NaN a NaN (a comparison with NaN is false).
+__device__ __forceinline__ float swiglu_act(float g, float u, Swiglu sw) {
+  if (sw.limit < 0.0f) return silu_mul(g, u);
+  const float L = sw.limit;
+  const float gc = g > L ? L : g;
+  const float uc = u < -L ? -L : (u > L ? L : u);
+  return gc / (1.0f + expf(-sw.alpha * gc)) * uc;
+}
+
 
 inline uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 

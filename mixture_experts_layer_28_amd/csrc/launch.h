@@ -69,11 +69,19 @@ hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,
                            hipStream_t st);
 
 // ---- experts ---------------------------------------------------------------
+// Activation of the gate+up epilogue: limit < 0 is the plain SiLU(g) * u;
+// otherwise the clipped form, gate clamped from above at limit, up to
+// [-limit, limit], swish with parameter alpha of the clamped gate.
+struct Swiglu {
+  float alpha = 1.0f;
+  float limit = -1.0f;
+};
+
 hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
                           int64_t I, int E, const void* w_gate,
                           const void* w_up, const void* w_down,
                           const uint32_t* offsets, void* act, void* y,
-                          hipStream_t st);
+                          hipStream_t st, Swiglu sw = Swiglu{});
 
 // 256x256-tile kernels for prefill-sized segments (bf16/f16, H and I
 // multiples of 8, 16-byte aligned, every per-expert weight matrix and 256
@@ -82,7 +90,7 @@ hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
                               int64_t I, int E, const void* w_gate,
                               const void* w_up, const void* w_down,
                               const uint32_t* offsets, void* act, void* y,
-                              hipStream_t st);
+                              hipStream_t st, Swiglu sw = Swiglu{});
 
 // One plain grouped NT product C[r, :] = A[r, :] . B[e]^T for the rows r of
 // segment e (A [N,K], B [E,NB,K], C [N,NB], all of dtype dt); rows past

@@ -381,6 +381,29 @@ int moe_experts_forward(const void* xd, int dt, int64_t N, int64_t H,
                     "moe_experts_forward");
 }
 
+int moe_experts_forward_clipped(const void* xd, int dt, int64_t N, int64_t H,
+                                int64_t I, int64_t E, const void* w_gate,
+                                const void* w_up, const void* w_down,
+                                const uint32_t* offsets, float alpha,
+                                float limit, void* act, void* y,
+                                void* stream) {
+  const int s = check_experts(xd, dt, N, H, I, E, w_gate, w_up, w_down,
+                              offsets, act, y);
+  if (s != MOE_OK) return s;
+  if (!std::isfinite(alpha))
+    return fail(MOE_ERR_INVALID_ARG, "moe_experts_forward_clipped: alpha must be finite");
+  if (!std::isfinite(limit) || !(limit >= 0.0f))
+    return fail(MOE_ERR_INVALID_ARG, "moe_experts_forward_clipped: limit must be finite and >= 0");
+  if (N == 0) return ok();
+  moe::Swiglu sw;
+  sw.alpha = alpha;
+  sw.limit = limit;
+  return hip_status(moe::launch_experts(xd, dt, N, H, I, (int)E, w_gate, w_up,
+                                        w_down, offsets, act, y,
+                                        (hipStream_t)stream, sw),
+                    "moe_experts_forward_clipped");
+}
+
 int moe_combine(const void* y, int dt, int64_t N, int64_t T, int64_t H,
                 int64_t top_k, const void* weights, int wdt,
                 const uint32_t* token_row, void* out, void* stream) {

@@ -151,6 +151,26 @@ def moe_experts_forward(xd, offsets, w_gate, w_up, w_down, act=None, y=None):
     return y
 
 
+def moe_experts_forward_clipped(xd, offsets, w_gate, w_up, w_down,
+                                alpha=1.702, limit=7.0, act=None, y=None):
+    """moe_experts_forward with the clipped SwiGLU activation (gate clamped
+    from above at ``limit``, up to [-limit, limit], swish with parameter
+    ``alpha``).  Returns y [N,H]."""
+    xd, offsets = _c(xd), _c(offsets)
+    w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
+    dev = _dev(xd, offsets, w_gate, w_up, w_down)
+    N, H = xd.shape
+    E, I = _experts_weights(w_gate, w_up, w_down, H, xd.dtype)
+    _index(offsets, (E + 1,), "offsets")
+    act = _out(act, (N, I), xd.dtype, dev, "act")
+    y = _out(y, (N, H), xd.dtype, dev, "y")
+    check(lib().moe_experts_forward_clipped(
+        _p(xd), _dt(xd, "xd"), N, H, I, E, _p(w_gate), _p(w_up), _p(w_down),
+        _p(offsets), float(alpha), float(limit), _p(act), _p(y),
+        _stream(dev)))
+    return y
+
+
 def moe_combine(y, weights, token_row, out=None):
     """Weighted merge.  y [N,H], weights [T,k], token_row [T,k] ->
     out [T,H]."""
@@ -410,4 +430,5 @@ __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_forward_sigmoid_grouped", "moe_selected_router_weights",
            "moe_selected_router_backward", "moe_experts_forward_training",
            "moe_combine_backward", "moe_experts_backward_workspace_size",
-           "moe_experts_backward", "moe_dispatch_backward", "_lib"]
+           "moe_experts_backward", "moe_dispatch_backward",
+           "moe_experts_forward_clipped", "_lib"]

@@ -331,3 +331,22 @@ def test_experts_backward_workspace_and_rejects():
     a = list(args)
     a[1] = 9
     assert L.moe_experts_backward(*a) == 3
+
+
+def test_experts_clipped_rejects():
+    L = _lib.lib()
+    base = [FAKE, 2, 100, 64, 32, 4, FAKE, FAKE, FAKE, FAKE, 1.702, 7.0,
+            FAKE, FAKE, None]
+    for i, v, st in [(10, float("inf"), 1), (10, float("nan"), 1),
+                     (11, -1.0, 1), (11, float("inf"), 1),
+                     (11, float("nan"), 1), (1, 9, 3), (6, None, 1),
+                     (12, None, 1)]:
+        a = list(base)
+        a[i] = v
+        assert L.moe_experts_forward_clipped(*a) == st, (i, v)
+        assert _last()
+    a = list(base)
+    a[2] = 0                          # N = 0 with valid options
+    assert L.moe_experts_forward_clipped(*a) == 0
+    a[11] = 0.0                       # limit 0 is allowed
+    assert L.moe_experts_forward_clipped(*a) == 0
