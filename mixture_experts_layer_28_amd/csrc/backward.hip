@@ -27,6 +27,8 @@
 // unaligned shapes use an LDS-tiled FP32 kernel (tn_kernel).  Elementwise
 // kernels do the SwiGLU forward and backward and the final add.
 
+#include <initializer_list>
+
 #include "device_common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -62,6 +64,54 @@ __global__ __launch_bounds__(256) void transpose_kernel(
     for (int i = ty; i < 64; i += 4) {
       const int64_t c = cb * 64 + i, r = rb * 64 + tx;
       if (r < R && c < C) dst[c * R + r] = tile[tx][i];
+    }
+    __syncthreads();
+  }
+}
+
+// LDS tile of 64 x 64 16-bit elements for the 16-byte transposes: the
+// 8-element vector v of row i sits in slot v ^ (i / 8 % 8), so that the
+// column gathers below (8 lanes on 8 row groups of one column block) hit
+// 32 different banks.
+__device__ __forceinline__ int tslot(int i, int v) { return v ^ ((i >> 3) & 7); }
+__device__ __forceinline__ uint16_t tread(const uint16_t (*tile)[64], int i,
+                                          int j) {
+  return tile[i][tslot(i, j >> 3) * 8 + (j & 7)];
+}
+
+// 16-bit elements, R and C multiples of 8, 16-byte aligned: 16-byte loads
+// of 8 consecutive columns into the LDS tile, then 16-byte stores of 8
+// consecutive rows of one column gathered from the tile; 8 neighbouring
+// lanes store the 8 row groups of one column, one 128-byte line.
+__global__ __launch_bounds__(256) void transpose16_kernel(
+    const uint16_t* __restrict__ in, uint16_t* __restrict__ out, int64_t E,
+    int64_t R, int64_t C) {
+  __shared__ uint16_t tile[64][64];
+  const int64_t nr = (R + 63) / 64, nc = (C + 63) / 64;
+  const int64_t total = E * nr * nc;
+  for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    const int64_t e = b / (nr * nc);
+    const int64_t r0 = ((b / nc) % nr) * 64, c0 = (b % nc) * 64;
+    const uint16_t* src = in + e * R * C;
+    uint16_t* dst = out + e * R * C;
+    // 64 rows x 8 vectors: thread t loads rows t/8 and t/8 + 32, vector t%8
+    for (int q = threadIdx.x; q < 512; q += 256) {
+      const int i = q / 8, v = q % 8;
+      const int64_t r = r0 + i, c = c0 + v * 8;
+      if (r < R && c < C)
+        *(u32x4*)&tile[i][tslot(i, v) * 8] = *(const u32x4*)(src + r * C + c);
+    }
+    __syncthreads();
+    // 64 columns x 8 vectors of rows: column j, rows 8w .. 8w+7
+    for (int q = threadIdx.x; q < 512; q += 256) {
+      const int j = q / 8, w = q % 8;
+      const int64_t c = c0 + j, r = r0 + w * 8;
+      if (c < C && r < R) {
+        uint16_t v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = tread(tile, w * 8 + t, j);
+        *(u32x4*)(dst + c * R + r) = *(const u32x4*)v;
+      }
     }
     __syncthreads();
   }
@@ -137,46 +187,166 @@ __global__ __launch_bounds__(256) void seg_pad_kernel(
   }
 }
 
+// The same per-expert transpose with 16-byte accesses (16-bit elements, C a
+// multiple of 8, 16-byte aligned).  A workgroup takes a strip of 64 rows of
+// one expert and a range of `ccols` columns; wave 0 finds the strip's
+// expert by a wave prefix sum of ceil(n_e / 64) over the experts.  Rows are
+// loaded as 16-byte column vectors into an LDS tile, and each column is
+// stored as 16-byte vectors of 8 consecutive rows of the expert (k a
+// multiple of 8, so every store is aligned), with zeros past n_e up to Kp:
+// the padding needs no separate pass.
+__global__ __launch_bounds__(256) void seg_transpose16_kernel(
+    const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+    const uint32_t* __restrict__ offsets, int E, int64_t N, int64_t C,
+    int64_t ccols, uint32_t ncg) {
+  __shared__ uint16_t tile[64][64];
+  __shared__ int64_t s_lo, s_n, s_k0, s_base;
+  __shared__ int s_found;
+  const uint32_t strip = blockIdx.x / ncg, cg = blockIdx.x % ncg;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (lane == 0) s_found = 0;
+    uint32_t base = 0;
+    for (int s0 = 0; s0 < E; s0 += 64) {
+      const int e = s0 + lane;
+      int64_t lo = 0, n = 0;
+      if (e < E) {
+        int64_t hi = offsets[e + 1];
+        hi = hi < N ? hi : N;
+        lo = offsets[e];
+        lo = lo < hi ? lo : hi;
+        n = hi - lo;
+      }
+      const uint32_t cnt = (uint32_t)((n + 63) / 64);
+      const uint32_t inc = wave_inclusive_sum(cnt, lane);
+      const uint32_t exc = inc - cnt;
+      const bool hit = strip >= base + exc && strip < base + inc;
+      if (__ballot(hit)) {
+        if (hit) {
+          s_lo = lo;
+          s_n = n;
+          s_k0 = (int64_t)(strip - base - exc) * 64;
+          s_base = C * (lo + 8 * (int64_t)e);
+          s_found = 1;
+        }
+        break;
+      }
+      base += __shfl(inc, 63, 64);
+    }
+  }
+  __syncthreads();
+  if (!s_found) return;
+  const int64_t lo = s_lo, n = s_n, k0 = s_k0, obase = s_base;
+  const int64_t kp = pad8(n);
+  const int64_t cend = (cg + 1) * ccols < C ? (cg + 1) * ccols : C;
+  for (int64_t c0 = cg * ccols; c0 < cend; c0 += 64) {
+    for (int q = threadIdx.x; q < 512; q += 256) {
+      const int i = q / 8, v = q % 8;
+      const int64_t k = k0 + i, c = c0 + v * 8;
+      if (k < n && c < C)
+        *(u32x4*)&tile[i][tslot(i, v) * 8] =
+            *(const u32x4*)(in + (lo + k) * C + c);
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < 512; q += 256) {
+      const int j = q / 8, w = q % 8;
+      const int64_t c = c0 + j, k = k0 + w * 8;
+      if (c < C && k < kp) {
+        uint16_t v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          v[t] = k + t < n ? tread(tile, w * 8 + t, j) : 0;
+        *(u32x4*)(out + obase + c * kp + k) = *(const u32x4*)v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---- elementwise -----------------------------------------------------------
+// NV consecutive elements per thread and step: 16-byte vectors when the
+// caller checked that every array is 16-byte aligned and n % NV == 0,
+// else NV = 1.
+template <int D, int NV>
+struct Chunk {
+  using S = typename Storage<D>::T;
+  S v[NV];
+  __device__ __forceinline__ void load(const S* p) {
+    if constexpr (NV * sizeof(S) == 16) *(u32x4*)v = *(const u32x4*)p;
+    else
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[i] = p[i];
+  }
+  __device__ __forceinline__ void store(S* p) const {
+    if constexpr (NV * sizeof(S) == 16) *(u32x4*)p = *(const u32x4*)v;
+    else
+#pragma unroll
+      for (int i = 0; i < NV; ++i) p[i] = v[i];
+  }
+};
+
 // act = SiLU(g) * u from the stored (rounded) g and u, as the forward's
 // fused epilogue computes it.
-template <int D>
+template <int D, int NV>
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(
     const typename Storage<D>::T* __restrict__ g,
     const typename Storage<D>::T* __restrict__ u,
     typename Storage<D>::T* __restrict__ a, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * 256)
-    a[i] = from_f32<D>(silu_mul(to_f32<D>(g[i]), to_f32<D>(u[i])));
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * NV; i < n;
+       i += (int64_t)gridDim.x * 256 * NV) {
+    Chunk<D, NV> cg, cu, ca;
+    cg.load(g + i);
+    cu.load(u + i);
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+      ca.v[q] = from_f32<D>(silu_mul(to_f32<D>(cg.v[q]), to_f32<D>(cu.v[q])));
+    ca.store(a + i);
+  }
 }
 
 // SwiGLU backward of a = SiLU(g) * u, s = sigmoid(g):
 //   dg = da * u * s * (1 + g * (1 - s)),  du = da * g * s
-template <int D>
+template <int D, int NV>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
     const typename Storage<D>::T* __restrict__ g,
     const typename Storage<D>::T* __restrict__ u,
     const typename Storage<D>::T* __restrict__ da,
     typename Storage<D>::T* __restrict__ dg,
     typename Storage<D>::T* __restrict__ du, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * 256) {
-    const float gv = to_f32<D>(g[i]), uv = to_f32<D>(u[i]);
-    const float d = to_f32<D>(da[i]);
-    const float s = 1.0f / (1.0f + expf(-gv));
-    dg[i] = from_f32<D>(d * uv * s * (1.0f + gv * (1.0f - s)));
-    du[i] = from_f32<D>(d * gv * s);
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * NV; i < n;
+       i += (int64_t)gridDim.x * 256 * NV) {
+    Chunk<D, NV> cg, cu, cd, og, ou;
+    cg.load(g + i);
+    cu.load(u + i);
+    cd.load(da + i);
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const float gv = to_f32<D>(cg.v[q]), uv = to_f32<D>(cu.v[q]);
+      const float d = to_f32<D>(cd.v[q]);
+      const float s = 1.0f / (1.0f + expf(-gv));
+      og.v[q] = from_f32<D>(d * uv * s * (1.0f + gv * (1.0f - s)));
+      ou.v[q] = from_f32<D>(d * gv * s);
+    }
+    og.store(dg + i);
+    ou.store(du + i);
   }
 }
 
-template <int D>
+template <int D, int NV>
 __global__ __launch_bounds__(256) void add_kernel(
     const typename Storage<D>::T* __restrict__ a,
     const typename Storage<D>::T* __restrict__ b,
     typename Storage<D>::T* __restrict__ c, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * 256)
-    c[i] = from_f32<D>(to_f32<D>(a[i]) + to_f32<D>(b[i]));
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * NV; i < n;
+       i += (int64_t)gridDim.x * 256 * NV) {
+    Chunk<D, NV> ca, cb, cc;
+    ca.load(a + i);
+    cb.load(b + i);
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+      cc.v[q] = from_f32<D>(to_f32<D>(ca.v[q]) + to_f32<D>(cb.v[q]));
+    cc.store(c + i);
+  }
 }
 
 // ---- combine backward ------------------------------------------------------
@@ -307,6 +477,18 @@ __global__ __launch_bounds__(256) void tn_kernel(
 template <typename W>
 hipError_t seg_transpose(const void* in, void* out, const uint32_t* offsets,
                          int E, int64_t N, int64_t C, hipStream_t st) {
+  // strips of 64 rows: at most ceil(N / 64) + E of them; columns in ranges
+  // of 512 per workgroup
+  const int64_t ccols = 512;
+  const int64_t ncg = (C + ccols - 1) / ccols;
+  const int64_t strips = (N + 63) / 64 + E;
+  if (sizeof(W) == 2 && C % 8 == 0 && strips * ncg < kMaxGrid * 8 &&
+      ((uintptr_t)in | (uintptr_t)out) % 16 == 0) {
+    hipLaunchKernelGGL(seg_transpose16_kernel, dim3((unsigned)(strips * ncg)),
+                       dim3(256), 0, st, (const uint16_t*)in, (uint16_t*)out,
+                       offsets, E, N, C, ccols, (uint32_t)ncg);
+    return hipGetLastError();
+  }
   const int64_t blocks = ((N + 63) / 64) * ((C + 63) / 64);
   hipLaunchKernelGGL((seg_transpose_kernel<W>), dim3(capped(blocks)),
                      dim3(256), 0, st, (const W*)in, (W*)out, offsets, E, N,
@@ -331,6 +513,12 @@ hipError_t transpose(const void* in, void* out, int64_t E, int64_t R,
 hipError_t transpose_dt(const void* in, int dt, void* out, int64_t E,
                         int64_t R, int64_t C, hipStream_t st) {
   if (dt == DT_F32) return transpose<uint32_t>(in, out, E, R, C, st);
+  if (R % 8 == 0 && C % 8 == 0 && ((uintptr_t)in | (uintptr_t)out) % 16 == 0) {
+    const int64_t blocks = E * ((R + 63) / 64) * ((C + 63) / 64);
+    hipLaunchKernelGGL(transpose16_kernel, dim3(capped(blocks)), dim3(256), 0,
+                       st, (const uint16_t*)in, (uint16_t*)out, E, R, C);
+    return hipGetLastError();
+  }
   return transpose<uint16_t>(in, out, E, R, C, st);
 }
 
@@ -375,12 +563,29 @@ hipError_t wgrad(const void* A, int dt, const void* B,
   return err;
 }
 
+// 16-byte vectors when every pointer is 16-byte aligned and n is a whole
+// number of vectors.
+template <int D>
+bool vec_ok(int64_t n, std::initializer_list<const void*> ps) {
+  constexpr int NV = 16 / sizeof(typename Storage<D>::T);
+  uintptr_t al = 0;
+  for (const void* p : ps) al |= (uintptr_t)p;
+  return n % NV == 0 && al % 16 == 0;
+}
+
 template <int D>
 hipError_t elementwise_fwd(const void* g, const void* u, void* a, int64_t n,
                            hipStream_t st) {
   using S = typename Storage<D>::T;
-  hipLaunchKernelGGL((swiglu_fwd_kernel<D>), dim3(capped((n + 255) / 256)),
-                     dim3(256), 0, st, (const S*)g, (const S*)u, (S*)a, n);
+  constexpr int NV = 16 / sizeof(S);
+  if (vec_ok<D>(n, {g, u, a}))
+    hipLaunchKernelGGL((swiglu_fwd_kernel<D, NV>),
+                       dim3(capped((n / NV + 255) / 256)), dim3(256), 0, st,
+                       (const S*)g, (const S*)u, (S*)a, n);
+  else
+    hipLaunchKernelGGL((swiglu_fwd_kernel<D, 1>),
+                       dim3(capped((n + 255) / 256)), dim3(256), 0, st,
+                       (const S*)g, (const S*)u, (S*)a, n);
   return hipGetLastError();
 }
 
@@ -388,9 +593,17 @@ template <int D>
 hipError_t elementwise_bwd(const void* g, const void* u, const void* da,
                            void* dg, void* du, int64_t n, hipStream_t st) {
   using S = typename Storage<D>::T;
-  hipLaunchKernelGGL((swiglu_bwd_kernel<D>), dim3(capped((n + 255) / 256)),
-                     dim3(256), 0, st, (const S*)g, (const S*)u,
-                     (const S*)da, (S*)dg, (S*)du, n);
+  constexpr int NV = 16 / sizeof(S);
+  if (vec_ok<D>(n, {g, u, da, dg, du}))
+    hipLaunchKernelGGL((swiglu_bwd_kernel<D, NV>),
+                       dim3(capped((n / NV + 255) / 256)), dim3(256), 0, st,
+                       (const S*)g, (const S*)u, (const S*)da, (S*)dg,
+                       (S*)du, n);
+  else
+    hipLaunchKernelGGL((swiglu_bwd_kernel<D, 1>),
+                       dim3(capped((n + 255) / 256)), dim3(256), 0, st,
+                       (const S*)g, (const S*)u, (const S*)da, (S*)dg,
+                       (S*)du, n);
   return hipGetLastError();
 }
 
@@ -398,8 +611,14 @@ template <int D>
 hipError_t elementwise_add(const void* a, const void* b, void* c, int64_t n,
                            hipStream_t st) {
   using S = typename Storage<D>::T;
-  hipLaunchKernelGGL((add_kernel<D>), dim3(capped((n + 255) / 256)),
-                     dim3(256), 0, st, (const S*)a, (const S*)b, (S*)c, n);
+  constexpr int NV = 16 / sizeof(S);
+  if (vec_ok<D>(n, {a, b, c}))
+    hipLaunchKernelGGL((add_kernel<D, NV>),
+                       dim3(capped((n / NV + 255) / 256)), dim3(256), 0, st,
+                       (const S*)a, (const S*)b, (S*)c, n);
+  else
+    hipLaunchKernelGGL((add_kernel<D, 1>), dim3(capped((n + 255) / 256)),
+                       dim3(256), 0, st, (const S*)a, (const S*)b, (S*)c, n);
   return hipGetLastError();
 }
 
