@@ -266,3 +266,52 @@ def test_full_size_sampled(name):
     g_rows = values(b["grad_xd"][rsel]).reshape(len(tokens), -1, H)
     want = round_to(g_rows.sum(axis=1), fmt)
     assert_close(values(r["dx"][sel]), want, fmt, "grad_x tokens")
+
+
+def test_misaligned_inputs_take_the_fallback_paths():
+    """Inputs 2 bytes off a 16-byte boundary (views into a larger buffer)
+    send the expert backward through its fallbacks: the FMA input-gradient
+    GEMM, the per-expert transposes with 2-byte accesses and their padding
+    pass, and scalar elementwise kernels; every stage still matches the
+    oracle on its own inputs."""
+    T, H, I, E, k = 150, 64, 96, 6, 2
+    wl = workloads.make("edge", T=T, H=H, I=I, E=E, k=k)
+    wl["logits"] = torch.nan_to_num(wl["logits"].float(), nan=0.0,
+                                    posinf=4.0, neginf=-4.0)
+    for name in ("x", "logits", "w_gate", "w_up", "w_down"):
+        wl[name] = wl[name].to(torch.bfloat16)
+    r = _run_chain(wl, k, 11)
+    fmt = "bf16"
+    d, cache, c = r["d"], r["cache"], r["c"]
+    N = d["xd"].shape[0]
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 != 0
+        return v
+
+    dexp = shifted(r["dexp"])
+    ws = torch.empty(moe.moe_experts_backward_workspace_size(
+        N, H, I, E, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    b = moe.moe_experts_backward(shifted(d["xd"]), d["offsets"], c["w_gate"],
+                                 c["w_up"], c["w_down"],
+                                 {key: shifted(cache[key])
+                                  for key in ("gate", "up", "act")},
+                                 dexp, workspace=ws)
+    b.update(_ws_parts(ws, N, H, I, E, torch.bfloat16))
+    torch.cuda.synchronize()
+    wg, wu, wd = (_np(c[key], fmt) for key in ("w_gate", "w_up", "w_down"))
+    off = u32(d["offsets"]).astype(np.int64)
+    xd = _np(d["xd"], fmt)
+    dact_r, ddown_r = down_backward(_np(r["dexp"], fmt),
+                                    _np(cache["act"], fmt), off, wd, fmt)
+    assert_close(values(b["dact"]), dact_r, fmt, "misaligned dact")
+    assert_close(values(b["grad_w_down"]), ddown_r, "f32",
+                 "misaligned grad_w_down")
+    for half, part, wt, key in (("dxg", "dg", wg, "grad_w_gate"),
+                                ("dxu", "du", wu, "grad_w_up")):
+        dx_r, dw_r = proj_backward(_np(b[part], fmt), xd, off, wt, fmt)
+        assert_close(values(b[half]), dx_r, fmt, "misaligned " + half)
+        assert_close(values(b[key]), dw_r, "f32", "misaligned " + key)
