@@ -76,6 +76,9 @@ def parse():
                    help="extension, not the benchmark: time one first-order "
                         "training step (forward and the backward chain) of "
                         "the workload; one JSON line")
+    p.add_argument("--clipped", action="store_true",
+                   help="extension, not the benchmark: time the expert stage "
+                        "with the plain and the clipped SwiGLU epilogue")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU work: print the kernel statistics of a "
                         "rocprofv3 --kernel-trace --stats run as markdown")
@@ -416,6 +419,53 @@ def train_step_bench(args):
         flush=True)
 
 
+def clipped_bench(args):
+    """Extension, not the benchmark: the expert stage of the workload with
+    the plain and with the clipped SwiGLU epilogue (alpha 1.702, limit 7) on
+    the same dispatched rows, alternating, torch events around each call."""
+    import statistics
+    import torch
+
+    import mixture_experts_layer_28_amd as moe
+    from mixture_experts_layer_28_amd import workloads
+
+    base, T = WORKLOADS[args.workload]
+    wl = workloads.make(base, T=T, device="cuda")
+    idx, _ = moe.moe_route(wl["logits"], wl["k"], wl["renorm"])
+    d = moe.moe_dispatch(wl["x"], idx, wl["E"])
+    N, H, I = d["xd"].shape[0], wl["H"], wl["I"]
+    act = torch.empty((N, I), dtype=d["xd"].dtype, device="cuda")
+    y = torch.empty((N, H), dtype=d["xd"].dtype, device="cuda")
+    calls = {
+        "plain": lambda: moe.moe_experts_forward(
+            d["xd"], d["offsets"], wl["w_gate"], wl["w_up"], wl["w_down"],
+            act=act, y=y),
+        "clipped": lambda: moe.moe_experts_forward_clipped(
+            d["xd"], d["offsets"], wl["w_gate"], wl["w_up"], wl["w_down"],
+            1.702, 7.0, act=act, y=y),
+    }
+    times = {name: [] for name in calls}
+    for _ in range(args.warmup):
+        for call in calls.values():
+            call()
+    for _ in range(args.steps):
+        for name, call in calls.items():
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            times[name].append(a.elapsed_time(b))
+    flop = 6 * N * H * I
+    out = {"extension": "clipped_swiglu", "workload": base, "N": N}
+    for name, ts in times.items():
+        ms = statistics.median(ts)
+        out[name] = {"ms": round(ms, 4),
+                     "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    print(json.dumps(out), flush=True)
+
+
 def summarize_trace(trace_dir):
     """Markdown table of a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -490,8 +540,17 @@ def cpu_baseline(wl):
             break
     dt = time.perf_counter() - t0
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": "%d of %d tokens (route, k experts, combine per token; "
                       "numpy float64), %.1f s" % (tokens, wl["T"], dt)}
 
@@ -512,6 +571,9 @@ def main():
         return
     if args.train:
         train_step_bench(args)
+        return
+    if args.clipped:
+        clipped_bench(args)
         return
     if args.copy_calibration:
         copy_calibration()

@@ -546,16 +546,20 @@ hipError_t tn_dt(const void* A, int dt, const void* B,
 // Weight gradient Cw[e] = A_e^T . B_e over each expert's rows (A [N,M],
 // B [N,NC] in dtype dt): on MFMA through per-expert transposed copies in
 // ta, tb when the shapes allow, else the FMA kernel.
+// tb_ready: tb already holds B's per-expert transpose (a previous call on
+// the same B took the MFMA path); *tb_used reports whether this call did.
 hipError_t wgrad(const void* A, int dt, const void* B,
                  const uint32_t* offsets, int64_t N, int E, int64_t M,
-                 int64_t NC, float* Cw, void* ta, void* tb, hipStream_t st) {
+                 int64_t NC, float* Cw, void* ta, void* tb, hipStream_t st,
+                 bool tb_ready = false, bool* tb_used = nullptr) {
   const uintptr_t al = (uintptr_t)ta | (uintptr_t)tb | (uintptr_t)Cw;
   const bool mfma = dt != DT_F32 && M % 8 == 0 && NC % 8 == 0 &&
                     al % 16 == 0 && 640 * (N + 8) < ((int64_t)1 << 31) &&
                     M <= INT32_MAX && NC <= INT32_MAX;
+  if (tb_used) *tb_used = mfma;
   if (!mfma) return tn_dt(A, dt, B, offsets, N, E, M, NC, Cw, st);
   hipError_t err = seg_transpose<uint16_t>(A, ta, offsets, E, N, M, st);
-  if (err == hipSuccess)
+  if (err == hipSuccess && !tb_ready)
     err = seg_transpose<uint16_t>(B, tb, offsets, E, N, NC, st);
   if (err == hipSuccess)
     err = launch_wgrad_big(ta, dt, N, (int)M, tb, (int)NC, E, offsets, Cw,
@@ -749,10 +753,14 @@ hipError_t launch_experts_backward(
     err = launch_grouped_nt(du, dt, N, I, wt, H, E, offsets, dxu, st);
   if (err == hipSuccess)
     err = MOE_BY_DT(dt, elementwise_add, dxg, dxu, dxd, N * H, st);
+  bool xd_in_tb = false;
   if (err == hipSuccess)
-    err = wgrad(dg, dt, xd, offsets, N, E, I, H, dwg, ta, tb, st);
+    err = wgrad(dg, dt, xd, offsets, N, E, I, H, dwg, ta, tb, st, false,
+                &xd_in_tb);
+  // xd's per-expert transpose from the gate's weight gradient is still in
+  // tb if that call made one (same stream, same shapes)
   if (err == hipSuccess)
-    err = wgrad(du, dt, xd, offsets, N, E, I, H, dwu, ta, tb, st);
+    err = wgrad(du, dt, xd, offsets, N, E, I, H, dwu, ta, tb, st, xd_in_tb);
   return err;
 }
 
