@@ -609,8 +609,9 @@ int moe_dispatch_backward(const void* grad_xd, int dt, int64_t N, int64_t T,
                           int64_t H, int64_t top_k,
                           const uint32_t* token_row, void* grad_x,
                           void* stream) {
-  // the combine kernel with unit weights; FAKE weights pointer satisfies
-  // the shared check, the launch passes none
+  // The combine kernel with unit weights.  check_combine only tests the
+  // weights pointer for null, so token_row stands in for it; the launch
+  // passes no weights.
   const int s = check_combine(grad_xd, dt, N, T, H, top_k, token_row, dt,
                               token_row, grad_x);
   if (s != MOE_OK) return s;
