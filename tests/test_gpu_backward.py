@@ -50,16 +50,27 @@ def _ws_parts(ws, N, H, I, E, dtype):
     return parts
 
 
-def _run_chain(wl, k, seed):
-    """The whole training chain on the GPU for a fixed selection (the
-    softmax router's) with FP32 router weights; returns every tensor."""
+def _run_chain(wl, k, seed, grouped=None):
+    """The whole training chain on the GPU for a fixed selection with FP32
+    router weights; returns every tensor.  The selection is the softmax
+    router's, or with ``grouped`` = (groups, selected_groups, scale) the
+    group-limited sigmoid router's (top-two group scores, renormalised),
+    whose training weights are sigmoid-scored."""
     dev = "cuda"
     c = {key: wl[key].to(dev) for key in ("x", "logits", "w_gate", "w_up",
                                           "w_down")}
     E = c["w_gate"].shape[0]
-    idx, _ = moe.moe_route(c["logits"], k, True)
-    w = moe.moe_selected_router_weights(c["logits"], idx, "softmax", True,
-                                        index_type="u32")
+    if grouped is None:
+        scoring, scale = "softmax", 1.0
+        idx, _ = moe.moe_route(c["logits"], k, True)
+    else:
+        groups, sel, scale = grouped
+        scoring = "sigmoid"
+        idx, _ = moe.moe_route_sigmoid_grouped(c["logits"], k, groups, sel,
+                                               group_top_two=True,
+                                               renormalize=True, scale=scale)
+    w = moe.moe_selected_router_weights(c["logits"], idx, scoring, True,
+                                        scale, index_type="u32")
     d = moe.moe_dispatch(c["x"], idx, E)
     cache = moe.moe_experts_forward_training(d["xd"], d["offsets"],
                                              c["w_gate"], c["w_up"],
@@ -78,11 +89,12 @@ def _run_chain(wl, k, seed):
     b.update(_ws_parts(ws, N, H, I, E, d["xd"].dtype))
     dx = moe.moe_dispatch_backward(b["grad_xd"], d["token_row"])
     dlogits = moe.moe_selected_router_backward(c["logits"], idx, dw,
-                                               "softmax", True,
+                                               scoring, True, scale,
                                                index_type="u32")
     torch.cuda.synchronize()
     return dict(c=c, idx=idx, w=w, d=d, cache=cache, out=out, dout=dout,
-                dexp=dexp, dw=dw, b=b, dx=dx, dlogits=dlogits)
+                dexp=dexp, dw=dw, b=b, dx=dx, dlogits=dlogits,
+                scoring=scoring, scale=scale)
 
 
 def _check_stages(r, fmt, what):
@@ -133,7 +145,7 @@ def _check_stages(r, fmt, what):
     # router backward on the GPU's weight gradient
     lg = values(c["logits"])
     dl_r = selected_router_backward(lg, u32(r["idx"]), values(r["dw"]),
-                                    "softmax", True, 1.0, fmt)
+                                    r["scoring"], True, r["scale"], fmt)
     assert_close(values(r["dlogits"]), dl_r, fmt, what + " grad_logits")
 
 
@@ -166,6 +178,39 @@ def test_f16_with_idle_experts():
     _check_stages(r, "f16", "idle experts")
     for key in ("grad_w_gate", "grad_w_up", "grad_w_down"):
         assert torch.count_nonzero(r["b"][key][8:]) == 0
+
+
+def _bf16_edge(T, H, I, E, k):
+    wl = workloads.make("edge", T=T, H=H, I=I, E=E, k=k)
+    wl["logits"] = torch.nan_to_num(wl["logits"].float(), nan=0.0,
+                                    posinf=4.0, neginf=-4.0)
+    for name in ("x", "logits", "w_gate", "w_up", "w_down"):
+        wl[name] = wl[name].to(torch.bfloat16)
+    return wl
+
+
+def test_sigmoid_grouped_selection():
+    """The chain behind the group-limited sigmoid router (8 groups of 8, 4
+    kept, scale 2.5) with sigmoid-scored training weights."""
+    wl = _bf16_edge(257, 128, 192, 64, 8)
+    r = _run_chain(wl, 8, 21, grouped=(8, 4, 2.5))
+    _check_stages(r, "bf16", "sigmoid grouped")
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(16, 256, 128, 32, 4),
+                                       (5, 64, 64, 128, 8)])
+def test_decode_sized(T, H, I, E, k):
+    """Fewer rows than 96 per expert: the NT products take the 32-row
+    decode tiles; the weight gradients have many tiny or empty experts."""
+    wl = _bf16_edge(T, H, I, E, k)
+    r = _run_chain(wl, k, T)
+    _check_stages(r, "bf16", "decode T=%d E=%d" % (T, E))
+
+
+def test_single_expert():
+    wl = _bf16_edge(300, 64, 128, 1, 1)
+    r = _run_chain(wl, 1, 2)
+    _check_stages(r, "bf16", "one expert")
 
 
 def test_staged_dispatch_backward_is_combine_with_unit_weights():
