@@ -214,6 +214,18 @@ int moe_forward(const void* x, int dt, const void* logits, int ldt,
                 size_t workspace_bytes, void* stream);
 
 /*
+ * moe_forward_clipped - moe_forward with the clipped SwiGLU activation of
+ * moe_experts_forward_clipped (alpha finite, limit finite and >= 0,
+ * MOE_ERR_INVALID_ARG otherwise).  Workspace and limits as moe_forward.
+ */
+int moe_forward_clipped(const void* x, int dt, const void* logits, int ldt,
+                        int64_t T, int64_t H, int64_t I, int64_t E,
+                        int64_t top_k, int renormalize, float alpha,
+                        float limit, const void* w_gate, const void* w_up,
+                        const void* w_down, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * moe_route_sigmoid_grouped - group-limited sigmoid routing (guide,
  * section 10 "group-limited sigmoid MoE routing": route_sigmoid_grouped
  * with GroupRoutingOptions).
@@ -453,7 +465,8 @@ int moe_dispatch_backward(const void* grad_xd, int dt, int64_t N, int64_t T,
  *
  * events: `count` hipEvent_t handles created by the caller (hipEventCreate),
  * or NULL with count 0 to switch recording off.  While set, every
- * moe_forward and moe_forward_sigmoid_grouped call on this thread records
+ * moe_forward, moe_forward_clipped and moe_forward_sigmoid_grouped call
+ * on this thread records
  * events[0] on its stream before its first kernel and events[i] right
  * after its i-th kernel, so the elapsed time between events[i-1] and
  * events[i] is kernel i.  The kernels of both forwards, in order: 1 route

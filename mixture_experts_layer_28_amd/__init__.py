@@ -13,7 +13,8 @@ from .ops import (moe_combine, moe_combine_backward, moe_dispatch,
                   moe_experts_backward, moe_experts_backward_workspace_size,
                   moe_experts_forward, moe_experts_forward_clipped,
                   moe_experts_forward_training,
-                  moe_forward, moe_forward_sigmoid_grouped,
+                  moe_forward, moe_forward_clipped,
+                  moe_forward_sigmoid_grouped,
                   moe_forward_workspace_size, moe_route,
                   moe_route_sigmoid_grouped, moe_selected_router_backward,
                   moe_selected_router_weights)
@@ -25,4 +26,4 @@ __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_selected_router_backward", "moe_experts_forward_training",
            "moe_combine_backward", "moe_experts_backward_workspace_size",
            "moe_experts_backward", "moe_dispatch_backward",
-           "moe_experts_forward_clipped"]
+           "moe_experts_forward_clipped", "moe_forward_clipped"]

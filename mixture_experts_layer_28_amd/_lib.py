@@ -38,6 +38,9 @@ SIGNATURES = {
                                          _INT]),
     "moe_forward": (_INT, [_P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                            _INT, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_forward_clipped": (_INT, [_P, _INT, _P, _INT, _I64, _I64, _I64, _I64,
+                                   _I64, _INT, _F32, _F32, _P, _P, _P, _P, _P,
+                                   _SZ, _P]),
     "moe_route_sigmoid_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _I64, _I64,
                                          _I64, _INT, _INT, _F32, _P, _P,
                                          _P]),

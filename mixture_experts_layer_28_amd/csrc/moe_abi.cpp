@@ -234,7 +234,7 @@ int run_forward(const char* f, const void* x, int dt, int ldt, int64_t T,
                 int64_t H, int64_t I, int64_t E, int64_t top_k,
                 const void* w_gate, const void* w_up, const void* w_down,
                 void* out, void* workspace, size_t workspace_bytes,
-                void* stream, Route route) {
+                void* stream, Route route, moe::Swiglu sw = moe::Swiglu{}) {
   // x stands in for the workspace-resident offsets/act/y buffers here;
   // the workspace itself is checked below.
   int s = check_experts(x, dt, T * top_k, H, I, E, w_gate, w_up, w_down, x, x, x);
@@ -281,7 +281,7 @@ int run_forward(const char* f, const void* x, int dt, int ldt, int64_t T,
   if (err != hipSuccess) return hip_status(err, what);
   moe::timing_mark(4, st);
   err = moe::launch_experts(xd, dt, N, H, I, (int)E, w_gate, w_up, w_down,
-                            offsets, act, y, st);
+                            offsets, act, y, st, sw);
   std::snprintf(what, sizeof(what), "%s(experts)", f);
   if (err != hipSuccess) return hip_status(err, what);
   moe::timing_mark(6, st);
@@ -443,6 +443,31 @@ int moe_forward(const void* x, int dt, const void* logits, int ldt,
         return moe::launch_route(logits, ldt, T, (int)E, (int)top_k,
                                  renormalize ? 1 : 0, idx, w, st);
       });
+}
+
+int moe_forward_clipped(const void* x, int dt, const void* logits, int ldt,
+                        int64_t T, int64_t H, int64_t I, int64_t E,
+                        int64_t top_k, int renormalize, float alpha,
+                        float limit, const void* w_gate, const void* w_up,
+                        const void* w_down, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const int s = check_route(logits, ldt, T, E, top_k, workspace, workspace);
+  if (s != MOE_OK) return s;
+  if (!std::isfinite(alpha))
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward_clipped: alpha must be finite");
+  if (!std::isfinite(limit) || !(limit >= 0.0f))
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward_clipped: limit must be finite and >= 0");
+  moe::Swiglu sw;
+  sw.alpha = alpha;
+  sw.limit = limit;
+  return run_forward(
+      "moe_forward_clipped", x, dt, ldt, T, H, I, E, top_k, w_gate, w_up,
+      w_down, out, workspace, workspace_bytes, stream,
+      [&](uint32_t* idx, void* w, hipStream_t st) {
+        return moe::launch_route(logits, ldt, T, (int)E, (int)top_k,
+                                 renormalize ? 1 : 0, idx, w, st);
+      },
+      sw);
 }
 
 int moe_route_sigmoid_grouped(const void* logits, int ldt, int64_t T,

@@ -213,6 +213,30 @@ def moe_forward(x, logits, w_gate, w_up, w_down, top_k, renormalize=True,
     return out
 
 
+def moe_forward_clipped(x, logits, w_gate, w_up, w_down, top_k,
+                        renormalize=True, alpha=1.702, limit=7.0, out=None,
+                        workspace=None):
+    """moe_forward with the clipped SwiGLU activation, one call."""
+    x, logits = _c(x), _c(logits)
+    w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
+    dev = _dev(x, logits, w_gate, w_up, w_down)
+    T, H = x.shape
+    E, I = _experts_weights(w_gate, w_up, w_down, H, x.dtype)
+    if logits.shape != (T, E):
+        raise ValueError("logits must be [T, E]")
+    workspace, ws_bytes = _workspace(
+        workspace,
+        moe_forward_workspace_size(T, H, I, E, top_k, x.dtype, logits.dtype),
+        dev)
+    out = _out(out, (T, H), x.dtype, dev, "out")
+    check(lib().moe_forward_clipped(
+        _p(x), _dt(x, "x"), _p(logits), _dt(logits, "logits"), T, H, I, E,
+        top_k, int(bool(renormalize)), float(alpha), float(limit),
+        _p(w_gate), _p(w_up), _p(w_down), _p(out), _p(workspace), ws_bytes,
+        _stream(dev)))
+    return out
+
+
 def _bias(bias, E, dev):
     """The optional FP32 correction bias [E] (None: no correction)."""
     if bias is None:
@@ -431,4 +455,4 @@ __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_selected_router_backward", "moe_experts_forward_training",
            "moe_combine_backward", "moe_experts_backward_workspace_size",
            "moe_experts_backward", "moe_dispatch_backward",
-           "moe_experts_forward_clipped", "_lib"]
+           "moe_experts_forward_clipped", "moe_forward_clipped", "_lib"]

@@ -350,3 +350,18 @@ def test_experts_clipped_rejects():
     assert L.moe_experts_forward_clipped(*a) == 0
     a[11] = 0.0                       # limit 0 is allowed
     assert L.moe_experts_forward_clipped(*a) == 0
+
+
+def test_forward_clipped_rejects():
+    L = _lib.lib()
+    ws = L.moe_forward_workspace_size(64, 128, 256, 8, 2, 0, 0)
+    args = [FAKE, 0, FAKE, 0, 64, 128, 256, 8, 2, 1, 1.702, 7.0, FAKE, FAKE,
+            FAKE, FAKE, 0x10000, ws, None]
+    for i, v in [(10, float("nan")), (11, -0.5), (11, float("inf")),
+                 (17, ws - 1), (16, 0x10010), (8, 0), (12, None)]:
+        a = list(args)
+        a[i] = v
+        assert L.moe_forward_clipped(*a) == 1, (i, v)
+    a = list(args)
+    a[4] = 0
+    assert L.moe_forward_clipped(*a) == 0

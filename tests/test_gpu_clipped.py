@@ -93,3 +93,31 @@ def test_full_size_sampled_rows():
                            clip=(alpha, limit))
             assert_close(values(y[r:r + 1]), want, "bf16",
                          "row %d L=%g" % (r, limit))
+
+
+def test_forward_clipped_one_call_equals_staged():
+    """moe_forward_clipped is route -> dispatch -> clipped experts ->
+    combine on one stream, bit for bit, and matches the oracle."""
+    wl = workloads.make("edge", T=300, H=128, I=192, E=8, k=2)
+    wl["logits"] = torch.nan_to_num(wl["logits"].float(), nan=0.0,
+                                    posinf=4.0, neginf=-4.0)
+    c = {key: wl[key].to(torch.bfloat16).cuda()
+         for key in ("x", "logits", "w_gate", "w_up", "w_down")}
+    one = moe.moe_forward_clipped(c["x"], c["logits"], c["w_gate"],
+                                  c["w_up"], c["w_down"], 2, True, 1.702,
+                                  0.5)
+    idx, w = moe.moe_route(c["logits"], 2, True)
+    d = moe.moe_dispatch(c["x"], idx, 8)
+    y = moe.moe_experts_forward_clipped(d["xd"], d["offsets"], c["w_gate"],
+                                        c["w_up"], c["w_down"], 1.702, 0.5)
+    staged = moe.moe_combine(y, w, d["token_row"])
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), staged.view(torch.int16))
+    tn = lambda t: workloads.to_numpy(t.cpu(), "bf16")  # noqa: E731
+    idx_r, w_r = route(tn(c["logits"]), 2, True, "bf16")
+    d_r = dispatch(tn(c["x"]), idx_r, 8)
+    y_r = experts(d_r["xd"], d_r["offsets"], tn(c["w_gate"]), tn(c["w_up"]),
+                  tn(c["w_down"]), "bf16", clip=(1.702, 0.5))
+    from oracle.moe import combine
+    out_r = combine(y_r, w_r, d_r["token_row"], "bf16")
+    assert_close(values(one), out_r, "bf16", "forward clipped")
