@@ -30,7 +30,8 @@
 // selected_groups groups beat it (counted over the row's group scores).
 // Top-k then takes k rounds of a 64-bit key maximum over the kept experts,
 // as in the softmax router; chosen ids go to LDS so that every lane can form
-// the slot-ordered renormalising sum.
+// the slot-ordered renormalising sum.  When the groups are whole lanes
+// (route_sigmoid_lane_kernel) the group stage runs in registers instead.
 //
 // Rows are walked in a grid-stride loop, so the grid stays a fixed size
 // whatever T is, and every barrier is reached by all threads of a block.
@@ -226,6 +227,138 @@ __global__ __launch_bounds__(256) void route_sigmoid_kernel(
   }
 }
 
+// Lane-aligned groups: E == G * PL and each group is L = gsz / PL whole
+// lanes (L a power of two).  Every step then stays in registers: a lane's
+// top two, merged over its group's L lanes by butterfly shuffles; each
+// group's rank counted over the other groups' scores fetched by shuffles;
+// the k rounds as above; the chosen experts' sigmoid values broadcast slot
+// by slot from their owner lanes, so every lane forms the slot-ordered
+// renormalising sum.  No LDS and no barriers.
+template <int LDT, int G, int PL, bool VEC>
+__global__ __launch_bounds__(256) void route_sigmoid_lane_kernel(
+    const typename Storage<LDT>::T* __restrict__ logits,
+    const float* __restrict__ bias, int64_t T, int E, int k,
+    GroupRouting o, int L, uint32_t* __restrict__ idx,
+    typename Storage<LDT>::T* __restrict__ w) {
+  using S = typename Storage<LDT>::T;
+  constexpr int R = 256 / G;
+  const int lane = threadIdx.x % G;
+  const int first = (int)(threadIdx.x % 64) - lane;  // the row's first lane
+  const int e0 = lane * PL;
+  const int g = lane / L;  // this lane's group
+
+  for (int64_t row = (int64_t)blockIdx.x * R + threadIdx.x / G; row < T;
+       row += (int64_t)gridDim.x * R) {
+    const S* src = logits + row * (int64_t)E + e0;
+    float v[PL];
+    if constexpr (VEC) {
+      constexpr int NE = 16 / sizeof(S);
+      static_assert(PL % NE == 0, "whole vectors per lane");
+#pragma unroll
+      for (int q = 0; q < PL / NE; ++q) {
+        S tmp[NE];
+        *(u32x4*)tmp = *(const u32x4*)(src + q * NE);
+#pragma unroll
+        for (int i = 0; i < NE; ++i) v[q * NE + i] = to_f32<LDT>(tmp[i]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < PL; ++m) v[m] = to_f32<LDT>(src[m]);
+    }
+    float sg[PL], c[PL];
+    int bad = 0;
+    float a = -INFINITY, b = -INFINITY;  // this lane's two largest c
+#pragma unroll
+    for (int m = 0; m < PL; ++m) {
+      sg[m] = sigmoid_f32(v[m]);
+      c[m] = bias ? sg[m] + bias[e0 + m] : sg[m];
+      bad |= __builtin_isnan(c[m]);
+      if (c[m] > a) {
+        b = a;
+        a = c[m];
+      } else if (c[m] > b) {
+        b = c[m];
+      }
+    }
+    // the group's two largest: merge the pairs of its L lanes
+    for (int off = 1; off < L; off <<= 1) {
+      const float a2 = __shfl_xor(a, off, 64), b2 = __shfl_xor(b, off, 64);
+      if (a2 > a) {
+        b = fmaxf(a, b2);
+        a = a2;
+      } else {
+        b = fmaxf(b, a2);
+      }
+    }
+    const float score = o.top_two ? a + b : a;
+    bad |= __builtin_isnan(score);
+    int beat = 0;
+    for (int h = 0; h < o.groups; ++h) {
+      const float y = __shfl(score, first + h * L, 64);
+      beat += (y > score) || (y == score && h < g);
+    }
+    const bool kept = beat < o.selected;
+    bad = group_or<G>(bad);
+
+    uint32_t* idx_row = idx + row * (int64_t)k;
+    S* w_row = w + row * (int64_t)k;
+    if (bad) {
+      for (int j = lane; j < k; j += G) {
+        idx_row[j] = (uint32_t)j;
+        w_row[j] = from_f32<LDT>(__builtin_nanf(""));
+      }
+      continue;
+    }
+    uint64_t key[PL];
+#pragma unroll
+    for (int m = 0; m < PL; ++m)
+      key[m] = kept ? make_key(c[m], (uint32_t)(e0 + m)) : 0ull;
+    uint64_t kj[PL];
+#pragma unroll
+    for (int m = 0; m < PL; ++m) kj[m] = 0ull;
+    uint64_t prev = ~0ull;
+    float den = 0.0f;
+    float sv[PL];
+#pragma unroll
+    for (int m = 0; m < PL; ++m) sv[m] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int m = 0; m < PL; ++m)
+        if (key[m] < prev && key[m] > best) best = key[m];
+      best = group_max_u64<G>(best);
+      prev = best;
+      // the chosen expert's sigmoid value, from the lane that holds it
+      const uint32_t id = 0xffffffffu - (uint32_t)best;
+      const int m_id = (int)(id % PL);
+      float mine = 0.0f;
+#pragma unroll
+      for (int m = 0; m < PL; ++m)
+        if (m == m_id) mine = sg[m];
+      const float sj = __shfl(mine, first + (int)(id / PL), 64);
+      den += sj;
+      if (lane == (j % G)) {
+#pragma unroll
+        for (int m = 0; m < PL; ++m)
+          if (m == j / G) {
+            kj[m] = best;
+            sv[m] = sj;
+          }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < PL; ++m) {
+      const int j = lane + G * m;
+      if (j < k) {
+        float x = sv[m];
+        if (o.renorm) x = x / den;
+        idx_row[j] = 0xffffffffu - (uint32_t)kj[m];
+        w_row[j] = from_f32<LDT>(x * o.scale);
+      }
+    }
+  }
+}
+
 template <int LDT, int G, int PL>
 hipError_t launch_sg(const void* logits, const float* bias, int64_t T, int E,
                      int k, const GroupRouting& o, uint32_t* idx, void* w,
@@ -236,6 +369,19 @@ hipError_t launch_sg(const void* logits, const float* bias, int64_t T, int E,
   const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
   const bool vec = (PL * sizeof(S)) % 16 == 0 && E == G * PL &&
                    (uintptr_t)logits % 16 == 0;
+  // lane-aligned groups: whole lanes per group, a power of two of them
+  const int L = o.gsz / PL;
+  if (E == G * PL && o.gsz % PL == 0 && (L & (L - 1)) == 0) {
+    if (vec)
+      hipLaunchKernelGGL((route_sigmoid_lane_kernel<LDT, G, PL, true>), grid,
+                         dim3(256), 0, st, (const S*)logits, bias, T, E, k, o,
+                         L, idx, (S*)w);
+    else
+      hipLaunchKernelGGL((route_sigmoid_lane_kernel<LDT, G, PL, false>), grid,
+                         dim3(256), 0, st, (const S*)logits, bias, T, E, k, o,
+                         L, idx, (S*)w);
+    return hipGetLastError();
+  }
   if (vec)
     hipLaunchKernelGGL((route_sigmoid_kernel<LDT, G, PL, true>), grid,
                        dim3(256), 0, st, (const S*)logits, bias, T, E, k, o,
