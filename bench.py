@@ -415,7 +415,16 @@ def train_step_bench(args):
         "experts_bwd_tflops": round(12 * N * H * I /
                                     (per["experts_bwd"] * 1e-3) / 1e12, 1),
         "experts_fwd_tflops": round(6 * N * H * I /
-                                    (per["experts_fwd"] * 1e-3) / 1e12, 1)}),
+                                    (per["experts_fwd"] * 1e-3) / 1e12, 1),
+        # the expert backward as a whole (its GEMMs, transposes and
+        # elementwise kernels) against the dense bf16 MFMA peak
+        "roofline": {"bound": "mfma", "kernel": "experts_bwd",
+                     "achieved": round(12 * N * H * I /
+                                       (per["experts_bwd"] * 1e-3) / 1e12, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(12 * N * H * I /
+                                   (per["experts_bwd"] * 1e-3) / 1e12 /
+                                   PEAK_BF16_TFLOPS, 4)}}),
         flush=True)
 
 
