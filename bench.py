@@ -79,6 +79,10 @@ def parse():
     p.add_argument("--clipped", action="store_true",
                    help="extension, not the benchmark: time the expert stage "
                         "with the plain and the clipped SwiGLU epilogue")
+    p.add_argument("--cold-cache", action="store_true",
+                   help="extension, not the benchmark: the forward with the "
+                        "Infinity Cache flushed before every step; per-kernel "
+                        "HBM rates")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU work: print the kernel statistics of a "
                         "rocprofv3 --kernel-trace --stats run as markdown")
@@ -475,6 +479,63 @@ def clipped_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def cold_cache_bench(args):
+    """Extension, not the benchmark: the forward with the 256 MB Infinity
+    Cache flushed before every step (a 1 GB fill, outside the events), so
+    each kernel's bytes come from HBM; per-kernel times from the library's
+    timing events, rates against the algorithmic bytes."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_28_amd as moe
+    from mixture_experts_layer_28_amd import _lib, workloads
+
+    dev = torch.device("cuda:0")
+    base, T = WORKLOADS[args.workload]
+    wl = workloads.make(base, T=T, device=dev)
+    T, H, I, E, k = wl["T"], wl["H"], wl["I"], wl["E"], wl["k"]
+    x, logits = wl["x"], wl["logits"]
+    idx, _ = moe.moe_route(logits, k, wl["renorm"])
+    d = moe.moe_dispatch(x, idx, E)
+    counts = np.diff(d["offsets"].cpu().numpy().astype(np.int64))
+    del d, idx
+    ws = torch.empty(moe.moe_forward_workspace_size(T, H, I, E, k, x.dtype),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    L = _lib.lib()
+    per = {name: [] for name in KERNELS}
+    for i in range(args.warmup + args.steps):
+        flush.fill_(i & 0xff)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        stream = torch.cuda.current_stream(dev)
+        for ev in evs:
+            ev.record(stream)
+        handles = (_lib.ctypes.c_void_p * 8)(*[ev.cuda_event for ev in evs])
+        _lib.check(L.moe_set_timing_events(handles, 8))
+        moe.moe_forward(x, logits, wl["w_gate"], wl["w_up"], wl["w_down"], k,
+                        wl["renorm"], out=out, workspace=ws)
+        _lib.check(L.moe_set_timing_events(None, 0))
+        torch.cuda.synchronize(dev)
+        if i >= args.warmup:
+            for j, name in enumerate(KERNELS):
+                per[name].append(evs[j].elapsed_time(evs[j + 1]))
+    alg = algorithmic(wl, counts)
+    stages = {}
+    for name in KERNELS:
+        ms = sorted(per[name])[len(per[name]) // 2]
+        st = {"ms": round(ms, 5),
+              "gbs": round(alg[name]["bytes"] / (ms * 1e-3) / 1e9, 1)}
+        st["hbm_frac"] = round(st["gbs"] / PEAK_HBM_GBS, 4)
+        if "flop" in alg[name]:
+            st["tflops"] = round(alg[name]["flop"] / (ms * 1e-3) / 1e12, 1)
+        stages[name] = st
+    step_ms = sum(st["ms"] for st in stages.values())
+    print(json.dumps({"extension": "cold_cache", "workload": base, "T": T,
+                      "step_gpu_ms_sum_of_medians": round(step_ms, 4),
+                      "stages": stages}), flush=True)
+
+
 def summarize_trace(trace_dir):
     """Markdown table of a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -583,6 +644,9 @@ def main():
         return
     if args.clipped:
         clipped_bench(args)
+        return
+    if args.cold_cache:
+        cold_cache_bench(args)
         return
     if args.copy_calibration:
         copy_calibration()
