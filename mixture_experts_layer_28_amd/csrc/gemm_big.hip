@@ -31,6 +31,7 @@
 
 #include "gemm_common.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace moe {
@@ -40,6 +41,21 @@ constexpr int kBM = 320, kBN = 256, kBK = 64;
 constexpr int kFM = kBM / 4 / 16;                 // MFMA row tiles per wave, at most
 constexpr int kStage = (kBM + kBN) * kBK;         // elements of one LDS stage
 constexpr size_t kLds = 2 * kStage * 2;           // two stages of 16-bit data
+
+// Opt a kernel in to kLds bytes of dynamic LDS, once per device (the
+// attribute belongs to each device's copy of the kernel); `done` holds one
+// bit per device id below 64, set once the call succeeded there.
+inline hipError_t allow_lds(const void* fn, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLds);
+  if (err == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return err;
+}
 
 // WG: the weight-gradient form.  Per expert e with rows [lo, hi) of a
 // dispatch, Cw[e] [M, NB] (FP32) = A_e . B_e^T with A_e = A + (lo + 8e) * M
@@ -327,14 +343,9 @@ hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
                       const uint32_t* offsets, int64_t N, int K, int NB,
                       int E, int nseg, hipStream_t st, Swiglu sw = Swiglu{}) {
   using S = typename Storage<D>::T;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t err = hipFuncSetAttribute(
-        (const void*)gemm_big_kernel<D, GATEUP>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-    if (err != hipSuccess) return err;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};
+  hipError_t err = allow_lds((const void*)gemm_big_kernel<D, GATEUP>, attr);
+  if (err != hipSuccess) return err;
   const uint32_t ncol = cdiv(NB, GATEUP ? kBN / 2 : kBN);
   // sum over segments of ceil(rows / kBM) <= ceil(N / kBM) + nseg
   const uint32_t grid = tile_grid(ncol * (cdiv(N, kBM) + (uint32_t)nseg));
@@ -368,28 +379,20 @@ hipError_t launch_wgrad_big(const void* A, int dt, int64_t N, int M,
   const uint32_t grid = tile_grid((uint32_t)E * nmb * ncol);
   if (dt == DT_BF16) {
     using S = typename Storage<DT_BF16>::T;
-    static bool attr = false;
-    if (!attr) {
-      hipError_t err = hipFuncSetAttribute(
-          (const void*)gemm_big_kernel<DT_BF16, false, true>,
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-      if (err != hipSuccess) return err;
-      attr = true;
-    }
+    static std::atomic<uint64_t> attr{0};
+    hipError_t err =
+        allow_lds((const void*)gemm_big_kernel<DT_BF16, false, true>, attr);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL((gemm_big_kernel<DT_BF16, false, true>), dim3(grid),
                        dim3(512), kLds, st, (const S*)A, (const S*)B,
                        (const S*)B, (S*)nullptr, offsets, N, M, NC, E, ncol, 0,
                        Cw);
   } else {
     using S = typename Storage<DT_F16>::T;
-    static bool attr = false;
-    if (!attr) {
-      hipError_t err = hipFuncSetAttribute(
-          (const void*)gemm_big_kernel<DT_F16, false, true>,
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-      if (err != hipSuccess) return err;
-      attr = true;
-    }
+    static std::atomic<uint64_t> attr{0};
+    hipError_t err =
+        allow_lds((const void*)gemm_big_kernel<DT_F16, false, true>, attr);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL((gemm_big_kernel<DT_F16, false, true>), dim3(grid),
                        dim3(512), kLds, st, (const S*)A, (const S*)B,
                        (const S*)B, (S*)nullptr, offsets, N, M, NC, E, ncol, 0,

@@ -111,6 +111,31 @@ def test_balanced_row_blocks(R):
     assert_close(y_gpu, y_ref, fmt, "balanced blocks R=%d" % R)
 
 
+@pytest.mark.parametrize("H,I,fmt", [(40, 48, "bf16"), (104, 72, "bf16"),
+                                      (136, 200, "f16"), (520, 136, "bf16")])
+def test_short_segments_in_prefill_tiles(H, I, fmt):
+    """Prefill-regime segments of 1, 17, 64 and 65 rows next to a large one
+    (an empty expert between them): row blocks of one to five 16-row MFMA
+    tiles, so most waves hold no rows and only load; H and I give 1, 2, 3,
+    4 and 9 K stages of the two-stage LDS pipeline."""
+    rng = np.random.default_rng(H + I)
+    sizes = [1, 17, 64, 65, 0, 700]
+    E = len(sizes)
+    T = sum(sizes)
+    assert T >= 96 * E  # the prefill kernel's regime
+    x = round_to(rng.standard_normal((T, H)), fmt)
+    wg = round_to(rng.standard_normal((E, I, H)) / np.sqrt(H), fmt)
+    wu = round_to(rng.standard_normal((E, I, H)) / np.sqrt(H), fmt)
+    wd = round_to(rng.standard_normal((E, H, I)) / np.sqrt(I), fmt)
+    idx = np.repeat(np.arange(E, dtype=np.uint32), sizes)[:, None]
+    idx = idx[rng.permutation(T)]
+    d = dispatch(x, idx, E)
+    assert list(np.diff(d["offsets"])) == sizes
+    y_ref = experts(d["xd"], d["offsets"], wg, wu, wd, fmt)
+    y_gpu = _experts_gpu(d, wg, wu, wd, fmt)
+    assert_close(y_gpu, y_ref, fmt, "short segments H=%d I=%d" % (H, I))
+
+
 def test_largest_expert_count():
     """E = 16383 experts (the library's limit), a few rows each for a
     handful of them and none for the rest."""
