@@ -83,6 +83,9 @@ def parse():
                    help="extension, not the benchmark: the forward with the "
                         "Infinity Cache flushed before every step; per-kernel "
                         "HBM rates")
+    p.add_argument("--summarize-counters", metavar="PMC_DIR",
+                   help="print a table of a rocprofv3 --pmc run's counters "
+                        "per library kernel (no GPU work)")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU work: print the kernel statistics of a "
                         "rocprofv3 --kernel-trace --stats run as markdown")
@@ -555,6 +558,76 @@ def summarize_trace(trace_dir):
                     float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
 
 
+SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs each
+XCDS = 8         # ... in 8 XCDs
+
+
+def summarize_counters(run_dir):
+    """Markdown table of one rocprofv3 --pmc run: per library kernel, the
+    mean over its dispatches of each counter as rocprofv3 reports it (one
+    value per dispatch, summed over the counter's dimensions: GRBM_ counters
+    over the 8 XCDs, so GRBM_GUI_ACTIVE / 8 is the kernel's active cycles),
+    the mean dispatch duration from the same run's timestamps, and where the
+    counters allow it the MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over
+    the active cycles times the SIMDs), the bf16 MFMA FLOP
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) with its rate, the clock (active
+    cycles over the duration), and FETCH_SIZE / WRITE_SIZE in MB as counted
+    (KiB x 1024, before any copy calibration)."""
+    import csv
+    import glob
+    vals, meta = {}, {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                d, c = int(r["Dispatch_Id"]), r["Counter_Name"]
+                vals.setdefault((d, c), []).append(float(r["Counter_Value"]))
+                meta[d] = (r["Kernel_Name"], int(r["End_Timestamp"]) -
+                           int(r["Start_Timestamp"]))
+    per = {}
+    for (d, c), v in vals.items():
+        name = meta[d][0].replace("(anonymous namespace)::", "")
+        name = name.replace("void ", "").split("(")[0]
+        if not name.startswith("moe::"):
+            continue
+        x = sum(v)
+        k = per.setdefault(name, {"_d": {}})
+        k.setdefault(c, {})[d] = x
+        k["_d"][d] = meta[d][1]
+    counters = sorted({c for k in per.values() for c in k if c != "_d"})
+    derived = []
+    if {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"} <= set(counters):
+        derived.append("MFMA busy %")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in counters:
+        derived += ["bf16 MFMA TFLOP", "TFLOP/s"]
+    if "GRBM_GUI_ACTIVE" in counters:
+        derived.append("GHz")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        if c in counters:
+            derived.append(c + " MB")
+    cols = ["kernel", "dispatches", "mean us"] + counters + derived
+    print("| " + " | ".join(cols) + " |")
+    print("|" + "---|" * len(cols))
+    for name, k in sorted(per.items(), key=lambda kv: -sum(kv[1]["_d"].values())):
+        n = len(k["_d"])
+        us = sum(k["_d"].values()) / n / 1e3
+        mean = {c: sum(k[c].values()) / len(k[c]) for c in counters if c in k}
+        row = [name, str(n), "%.1f" % us] + ["%.4g" % mean[c] if c in mean
+                                             else "" for c in counters]
+        if "MFMA busy %" in derived:
+            row.append("%.1f" % (100.0 * mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0)
+                                 / (mean["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)))
+        if "TFLOP/s" in derived:
+            fl = mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512
+            row += ["%.4g" % (fl / 1e12), "%.0f" % (fl / (us * 1e-6) / 1e12)]
+        if "GHz" in derived:
+            row.append("%.2f" % (mean["GRBM_GUI_ACTIVE"] / XCDS / (us * 1e3)))
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c + " MB" in derived:
+                row.append("%.1f" % (mean.get(c, 0) * 1024 / 1e6))
+        print("| " + " | ".join(row) + " |")
+
+
 def recorded_traffic(key):
     """HBM bytes per launch recorded in profiles/traffic.json for `key`, if
     the kernel sources still hash to what they were when the counters were
@@ -632,6 +705,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.route_sweep:
         route_sweep()
