@@ -44,6 +44,63 @@
 namespace moe {
 namespace {
 
+// The plain tile map of locate_tile (BM-row blocks, the same logical order
+// and XCD ranges), run by each wavefront on its own and broadcast to its
+// lanes: the kernel then keeps no tile record in LDS and needs no barrier
+// before its K loop, so four of its workgroups fit the 160 KB of LDS of a
+// CU (the record pushed each one just past a quarter).
+__device__ inline TileInfo locate_tile_wave(uint32_t b,
+                                            const uint32_t* __restrict__ offsets,
+                                            int E, int64_t N, int BM,
+                                            uint32_t ncol, int nseg) {
+  const int lane = threadIdx.x & 63;
+  TileInfo t;
+  t.found = 0;
+  t.e = t.col = t.rows = 0;
+  t.lo = t.hi = t.row0 = 0;
+  uint32_t total = 0;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    int64_t lo, hi;
+    segment(offsets, s0 + lane, E, N, nseg, &lo, &hi);
+    const uint32_t cnt = (uint32_t)((hi - lo + BM - 1) / BM) * ncol;
+    total += __shfl(wave_inclusive_sum(cnt, lane), 63, 64);
+  }
+  const uint32_t per = (total + 7u) / 8u, local = b / 8u;
+  const uint32_t L = (b % 8u) * per + local;
+  if (local >= per || L >= total) return t;
+  uint32_t base = 0;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    int64_t lo, hi;
+    segment(offsets, s0 + lane, E, N, nseg, &lo, &hi);
+    const uint32_t nt = (uint32_t)((hi - lo + BM - 1) / BM);
+    const uint32_t cnt = nt * ncol;
+    const uint32_t inc = wave_inclusive_sum(cnt, lane);
+    const uint32_t exc = inc - cnt;
+    const bool hit = L >= base + exc && L < base + inc;
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      const int src = (int)__builtin_ctzll(m);
+      const int64_t slo = __shfl(lo, src, 64), shi = __shfl(hi, src, 64);
+      const uint32_t snt = __shfl(nt, src, 64), sexc = __shfl(exc, src, 64);
+      const uint32_t l = L - base - sexc;
+      constexpr uint32_t GM = 8;
+      const uint32_t grp = l / (GM * ncol), first = grp * GM;
+      const uint32_t gs = snt - first < GM ? snt - first : GM;
+      const uint32_t rem = l - grp * GM * ncol;
+      t.e = s0 + src;
+      t.lo = slo;
+      t.hi = shi;
+      t.col = (int)(rem / gs);
+      t.row0 = slo + (int64_t)(first + rem % gs) * BM;
+      t.rows = (int)(shi - t.row0 < BM ? shi - t.row0 : BM);
+      t.found = 1;
+      return t;
+    }
+    base += __shfl(inc, 63, 64);
+  }
+  return t;
+}
+
 template <int D, int BM, int BN, int WGM, bool GATEUP, bool NTW>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const typename Storage<D>::T* __restrict__ A,
@@ -64,13 +121,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 
   __shared__ __attribute__((aligned(16))) S As[2][BM * BK];
   __shared__ __attribute__((aligned(16))) S Bs[2][BN * BK];
-  __shared__ TileInfo ti;
 
   const int tid = threadIdx.x;
-  if (tid < 64)
-    locate_tile(blockIdx.x, gridDim.x, offsets, E, N, BM, ncol, nseg, &ti);
-  __syncthreads();
-  if (!ti.found) return;
+  const TileInfo ti =
+      locate_tile_wave(blockIdx.x, offsets, E, N, BM, ncol, nseg);
+  if (!ti.found) return;  // the same answer in every wavefront
   const int e = uniform(ti.e);
   const int64_t hi = uniform(ti.hi), row0 = uniform(ti.row0);
   const int64_t n0 = (int64_t)uniform(ti.col) * TCOLS;
