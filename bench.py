@@ -83,6 +83,10 @@ def parse():
                    help="extension, not the benchmark: the forward with the "
                         "Infinity Cache flushed before every step; per-kernel "
                         "HBM rates")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the forward captured once in a HIP graph "
+                        "and replayed per step (an extension field 'graph'; "
+                        "the headline value stays the eager forward)")
     p.add_argument("--summarize-counters", metavar="PMC_DIR",
                    help="print a table of a rocprofv3 --pmc run's counters "
                         "per library kernel (no GPU work)")
@@ -834,6 +838,24 @@ def main():
                 "traffic": recorded_traffic(args.workload + "/gateup_gemm"),
                 "kernel": "gateup_gemm"}
 
+    graph = None
+    if args.graph:
+        # the library enqueues only kernels, so the whole forward captures
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        g_el = time.perf_counter() - t1
+        graph = {"value": round(T * args.steps / g_el, 1),
+                 "ms_per_step": round(g_el / args.steps * 1e3, 4)}
+        del g
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl)
@@ -870,6 +892,8 @@ def main():
         "stages": stages,
         "cpu_baseline": cpu,
     }
+    if graph is not None:
+        line["graph"] = graph
     print(json.dumps(line), flush=True)
 
 
