@@ -10,8 +10,9 @@
 // wavefront's sequential job, which makes the order inside every expert
 // segment the stable (token, slot) order without global atomics:
 //   1. count:   per chunk, per expert: how many entries, and each entry's
-//               rank among the chunk's entries of the same expert (a ballot
-//               per distinct expert in each 64-entry group).
+//               rank among the chunk's entries of the same expert (lanes of
+//               a 64-entry group with equal expert ids are found with one
+//               ballot per bit of the id).
 //   2. scan:    one workgroup turns the [chunk][expert] counts into segment
 //               offsets and, in place, into each chunk's first row per expert.
 //   3. scatter: each token row is read once and written to its k rows
@@ -39,6 +40,9 @@ __global__ void dispatch_count_kernel(const uint32_t* __restrict__ idx,
   uint32_t* cnt = cnt_all + wv * nb;
   for (int b = lane; b < nb; b += 64) cnt[b] = 0u;
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // bits of a bin id (0..E): lanes holding the same bin are found by one
+  // ballot per bit, whatever the number of distinct bins in the group
+  const int nbits = 32 - __builtin_clz((unsigned)E | 1u);
   const int64_t i0 = c * chunk;
   const int64_t i1 = (i0 + chunk < N) ? i0 + chunk : N;
   for (int64_t g = i0; g < i1; g += 64) {
@@ -46,23 +50,21 @@ __global__ void dispatch_count_kernel(const uint32_t* __restrict__ idx,
     const bool valid = i < i1;
     uint32_t e = valid ? idx[i] : 0u;
     if (e > (uint32_t)E) e = (uint32_t)E;
-    uint64_t todo = __ballot(valid);
-    uint32_t rank = 0;
-    while (todo) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)e, leader);
-      const bool mine = valid && e == v;
-      const uint64_t m = __ballot(mine);
-      uint32_t old = 0;
-      if (lane == leader) {
-        old = cnt[v];
-        cnt[v] = old + (uint32_t)__popcll(m);
-      }
-      old = (uint32_t)__builtin_amdgcn_readlane((int)old, leader);
-      if (mine) rank = old + (uint32_t)__popcll(m & lt);
-      todo &= ~m;
+    uint64_t same = __ballot(valid);  // valid lanes whose bin equals e
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t m = __ballot(valid && ((e >> bit) & 1u));
+      same &= ((e >> bit) & 1u) ? m : ~m;
     }
-    if (valid) local_rank[i] = rank;
+    // the lowest lane of each bin adds the group's count to the chunk's
+    // and hands the previous count to the other lanes of its bin
+    const int leader = valid ? (int)__builtin_ctzll(same) : lane;
+    uint32_t old = 0;
+    if (valid && leader == lane) {
+      old = cnt[e];
+      cnt[e] = old + (uint32_t)__popcll(same);
+    }
+    old = (uint32_t)__shfl((int)old, leader, 64);
+    if (valid) local_rank[i] = old + (uint32_t)__popcll(same & lt);
   }
   for (int b = lane; b < nb; b += 64) table[c * nb + b] = cnt[b];
 }
