@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const typename Storage<D>::T* __restrict__ y, int64_t N, int64_t T,
     int64_t H, int k, const typename Storage<WD>::T* __restrict__ w,
     const uint32_t* __restrict__ token_row,
-    typename Storage<D>::T* __restrict__ out, int tpb) {
+    typename Storage<D>::T* __restrict__ out, int tpb, int64_t vchunk) {
   using S = typename Storage<D>::T;
   extern __shared__ uint32_t sm[];
   uint32_t* srow = sm;
@@ -89,10 +89,13 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
   __syncthreads();
   const int64_t vpr = H / NV;  // vectors per row (NV elements each)
-  const int64_t total = (int64_t)tpb * vpr;
+  // this block's vectors of each row: [v0, v0 + vlen) (blockIdx.y)
+  const int64_t v0 = (int64_t)blockIdx.y * vchunk;
+  const int64_t vlen = vpr - v0 < vchunk ? vpr - v0 : vchunk;
+  const int64_t total = (int64_t)tpb * vlen;
   for (int64_t q = threadIdx.x; q < total; q += blockDim.x) {
-    const int tl = (int)(q / vpr);
-    const int64_t v = q - (int64_t)tl * vpr;
+    const int tl = (int)(q / vlen);
+    const int64_t v = v0 + q - (int64_t)tl * vlen;
     const int64_t t = t0 + tl;
     if (t >= T) break;
     float acc[NV];
@@ -115,13 +118,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
 template <int D, int WD, int NV, bool NTL>
 void launch_ck(const void* y, int64_t N, int64_t T, int64_t H, int k,
                const void* w, const uint32_t* token_row, void* out,
-               dim3 grid, size_t lds, int tpb, hipStream_t st) {
+               dim3 grid, size_t lds, int tpb, int64_t vchunk,
+               hipStream_t st) {
   using S = typename Storage<D>::T;
   using SW = typename Storage<WD>::T;
 #define MOE_COMBINE(KC)                                                        \
   hipLaunchKernelGGL((combine_kernel<D, WD, NV, KC, NTL>), grid, dim3(256), lds, st, \
                      (const S*)y, N, T, H, k, (const SW*)w, token_row, (S*)out, \
-                     tpb)
+                     tpb, vchunk)
   switch (k) {
     case 1: MOE_COMBINE(1); break;
     case 2: MOE_COMBINE(2); break;
@@ -139,6 +143,7 @@ hipError_t launch_c(const void* y, int64_t N, int64_t T, int64_t H, int k,
                     hipStream_t st) {
   using S = typename Storage<D>::T;
   constexpr int NV = Vec<D>::n;
+  if (T <= 0 || H <= 0) return hipSuccess;  // nothing to launch
   const bool vec_ok = H % NV == 0 && ((uintptr_t)y % 16 == 0) &&
                       ((uintptr_t)out % 16 == 0);
   const int64_t vpr = vec_ok ? H / NV : H;
@@ -146,15 +151,28 @@ hipError_t launch_c(const void* y, int64_t N, int64_t T, int64_t H, int k,
   if (tpb < 1) tpb = 1;
   if (tpb * k > 2048) tpb = 2048 / k;
   if (tpb < 1) tpb = 1;
-  const dim3 grid((unsigned)((T + tpb - 1) / tpb));
+  // Few token blocks (decode-sized batches): split each row's vectors over
+  // grid.y so that about 256 workgroups share the loads, at least 64
+  // vectors per row each, instead of a few workgroups walking whole rows.
+  const int64_t nb = (T + tpb - 1) / tpb;
+  int64_t nvc = 1;
+  if (nb < 256) {
+    nvc = (256 + nb - 1) / nb;
+    const int64_t most = (vpr + 63) / 64;
+    if (nvc > most) nvc = most;
+    if (nvc < 1) nvc = 1;
+  }
+  const int64_t vchunk = (vpr + nvc - 1) / nvc;
+  nvc = (vpr + vchunk - 1) / vchunk;
+  const dim3 grid((unsigned)nb, (unsigned)nvc);
   const size_t lds = (size_t)tpb * k * 8;
   const bool stream = N * H * (int64_t)sizeof(S) > ((int64_t)128 << 20);
   if (vec_ok && stream)
-    launch_ck<D, WD, NV, true>(y, N, T, H, k, w, token_row, out, grid, lds, (int)tpb, st);
+    launch_ck<D, WD, NV, true>(y, N, T, H, k, w, token_row, out, grid, lds, (int)tpb, vchunk, st);
   else if (vec_ok)
-    launch_ck<D, WD, NV, false>(y, N, T, H, k, w, token_row, out, grid, lds, (int)tpb, st);
+    launch_ck<D, WD, NV, false>(y, N, T, H, k, w, token_row, out, grid, lds, (int)tpb, vchunk, st);
   else
-    launch_ck<D, WD, 1, false>(y, N, T, H, k, w, token_row, out, grid, lds, (int)tpb, st);
+    launch_ck<D, WD, 1, false>(y, N, T, H, k, w, token_row, out, grid, lds, (int)tpb, vchunk, st);
   (void)sizeof(S);
   return hipGetLastError();
 }

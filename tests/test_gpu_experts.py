@@ -169,13 +169,17 @@ def test_experts_zero_rows_for_trailing_segment():
 @pytest.mark.parametrize("T,H,k,fmt,wfmt", [
     (64, 128, 2, "f32", "f32"), (512, 256, 16, "f16", "f16"),
     (333, 72, 3, "bf16", "bf16"), (100, 13, 2, "bf16", "f32"),
-    (50, 7, 1, "f16", "bf16")])
+    (50, 7, 1, "f16", "bf16"),
+    # few tokens, long rows: each row's vectors split over several
+    # workgroups (ragged last chunk; fp32; the scalar path for odd H)
+    (5, 4104, 2, "bf16", "bf16"), (3, 2056, 8, "f32", "f32"),
+    (7, 1031, 4, "bf16", "bf16"), (40, 4096, 8, "bf16", "bf16")])
 def test_combine_stage(T, H, k, fmt, wfmt):
     rng = np.random.default_rng(T + H)
     N = T * k
     y = round_to(rng.standard_normal((N, H)), fmt)
     w = round_to(rng.random((T, k)), wfmt)
-    w[3] = np.nan
+    w[min(3, T - 1)] = np.nan
     token_row = rng.permutation(N).reshape(T, k).astype(np.uint32)
     out = moe.moe_combine(_tensor(y, fmt).cuda(), _tensor(w, wfmt).cuda(),
                           _u32(token_row).cuda())
