@@ -256,21 +256,26 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       // register set, so the matrix pipe has work while those reads land
       // (1-2 % faster).  With 5 row tiles the second register set does not
       // fit in 256 VGPRs, so that count keeps the plain order below.
+      // The last K step is peeled off: with it inside the loop, the branch
+      // that skips the barrier joins the barrier path just before the
+      // second-half MFMAs, and the wait counts merged at that join made
+      // them wait for the next stage's fragment reads as well.
       V fa0[FMC], fb0[FN], fa1[FMC], fb1[FN];
       read_frags(0, 0, fa0, fb0);
-      for (int kt = 0; kt < nk; ++kt) {
+      for (int kt = 0; kt + 1 < nk; ++kt) {
         const int st = kt & 1;
         read_frags(st, 1, fa1, fb1);
         mma(fa0, fb0);
-        if (kt + 1 < nk) {
-          wait_vmem();
-          __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
-          if (kt + 2 < nk) dma((kt + 2) * kBK, st);
-          read_frags(st ^ 1, 0, fa0, fb0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        wait_vmem();
+        __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
+        if (kt + 2 < nk) dma((kt + 2) * kBK, st);
+        read_frags(st ^ 1, 0, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
         mma(fa1, fb1);
       }
+      read_frags((nk - 1) & 1, 1, fa1, fb1);
+      mma(fa0, fb0);
+      mma(fa1, fb1);
     } else {
       for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
