@@ -276,6 +276,53 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       read_frags((nk - 1) & 1, 1, fa1, fb1);
       mma(fa0, fb0);
       mma(fa1, fb1);
+    } else if constexpr (FMC > 4) {
+      // Five row tiles: a second fragment set does not fit beside the 160
+      // accumulators in 256 VGPRs.  One set is reloaded in place for the
+      // next half while the current one is multiplied: the MFMAs of a half
+      // go column by column, each B fragment is reloaded right after its
+      // column, and each A fragment right after its MFMA of the last column.
+      // The barrier sits between the halves and the last K step is peeled,
+      // as above.
+      auto read_a = [&](int st, int half, int i) -> V {
+        const S* As = sm + st * kStage;
+        const int c = half * 4 + (lane >> 4);
+        const int r = tr0 + i * 16 + (lane & 15);
+        return *(const V*)&As[r * kBK + ((c ^ swz(r)) << 3)];
+      };
+      auto read_b = [&](int st, int half, int j) -> V {
+        const S* Bs = sm + st * kStage + kBM * kBK;
+        const int c = half * 4 + (lane >> 4);
+        const int r = brow(j);
+        return *(const V*)&Bs[r * kBK + ((c ^ swz(r)) << 3)];
+      };
+      V fa[FMC], fb[FN];
+      auto mma_cols = [&](int st2, int half2, bool reload) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int i = 0; i < FMC; ++i) {
+            acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
+            if (reload && j == FN - 1) fa[i] = read_a(st2, half2, i);
+          }
+          if (reload) fb[j] = read_b(st2, half2, j);
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < FMC; ++i) fa[i] = read_a(0, 0, i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = read_b(0, 0, j);
+      for (int kt = 0; kt + 1 < nk; ++kt) {
+        const int st = kt & 1;
+        mma_cols(st, 1, true);  // first half; fragments of the second
+        wait_vmem();
+        __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
+        if (kt + 2 < nk) dma((kt + 2) * kBK, st);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_cols(st ^ 1, 0, true);  // second half; fragments of the next
+      }
+      mma_cols((nk - 1) & 1, 1, true);
+      mma_cols(0, 0, false);
     } else {
       for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
