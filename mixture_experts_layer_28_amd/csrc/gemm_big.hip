@@ -281,7 +281,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       // accumulators in 256 VGPRs.  One set is reloaded in place for the
       // next half while the current one is multiplied: the MFMAs of a half
       // go column by column, each B fragment is reloaded right after its
-      // column, and each A fragment right after its MFMA of the last column.
+      // column, and each A fragment right after its MFMAs of the last two
+      // columns (taken row by row).
       // The barrier sits between the halves and the last K step is peeled,
       // as above.
       auto read_a = [&](int st, int half, int i) -> V {
@@ -299,13 +300,24 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       V fa[FMC], fb[FN];
       auto mma_cols = [&](int st2, int half2, bool reload) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < FN - 2; ++j) {
 #pragma unroll
-          for (int i = 0; i < FMC; ++i) {
+          for (int i = 0; i < FMC; ++i)
             acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
-            if (reload && j == FN - 1) fa[i] = read_a(st2, half2, i);
-          }
           if (reload) fb[j] = read_b(st2, half2, j);
+        }
+        // the last two columns row by row, so each A fragment is reloaded
+        // eight MFMAs before the next half needs it
+#pragma unroll
+        for (int i = 0; i < FMC; ++i) {
+#pragma unroll
+          for (int j = FN - 2; j < FN; ++j)
+            acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
+          if (reload) fa[i] = read_a(st2, half2, i);
+        }
+        if (reload) {
+          fb[FN - 2] = read_b(st2, half2, FN - 2);
+          fb[FN - 1] = read_b(st2, half2, FN - 1);
         }
       };
 #pragma unroll
