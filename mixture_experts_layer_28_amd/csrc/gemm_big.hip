@@ -26,8 +26,14 @@
 // * Two LDS stages of K = 64 (2 x 72 KB, one workgroup per CU) and one
 //   barrier per stage; the loads of stage k+2 go out right after the
 //   barrier that ends stage k, so they have a whole stage of MFMAs to land.
-// * Measured on MI355X: this kernel is bound by operand delivery into the
-//   CUs (global -> LDS), not by the MFMA or LDS-read rates.
+//   The second half of a stage is multiplied after that barrier from
+//   fragments read before it, while the next stage's first fragments are
+//   read (a second register set for up to 4 row tiles, in-place reloads for
+//   5), and the last stage is peeled so no branch merges those waits.
+// * Measured on MI355X: the matrix pipes are busy 50-67 % of the active
+//   cycles and the clock falls to 1.6-1.85 GHz under this load; the rest
+//   is operand delivery into the CUs (global -> LDS) and the per-stage
+//   barrier, not the MFMA or LDS-read rates.
 
 #include "gemm_common.h"
 
