@@ -6,10 +6,12 @@
 //
 // * Row blocks of up to 320 rows x 256 columns per workgroup of 8
 //   wavefronts in a 4 x 2 grid.  A segment of R rows is cut into
-//   ceil(R / 320) row blocks of equal size (+-1 row), so a segment a few rows
-//   longer than a multiple of 256 does not leave a thin last block that
-//   costs a whole pass over the weights; Mixtral-sized segments of about
-//   1000-1070 rows become 4 blocks of 246-267 rows.  The 16-row MFMA row
+//   ceil(R / 320) row blocks made of whole 32-row units dealt out evenly,
+//   so a segment a few rows longer than a multiple of 256 does not leave a
+//   thin last block that costs a whole pass over the weights, and no block
+//   leaves a matrix-pipe slot of its busiest SIMD idle; a Mixtral-sized
+//   segment of 1065 rows becomes blocks of 256, 288, 256 and 265 rows.  The
+//   16-row MFMA row
 //   tiles of a block are shared out over the 4 wave rows as evenly as
 //   possible (at most 5 each); a wave owns up to 80 x 128 outputs as
 //   v_mfma_f32_16x16x32 tiles with FP32 accumulators, two waves per SIMD.
@@ -69,7 +71,7 @@ inline hipError_t allow_lds(const void* fn, std::atomic<uint64_t>& done) {
 // hi - lo rounded up to a multiple of 8 with zeros past hi - lo (each
 // expert's rows transposed into one block whose rows are 16-byte aligned),
 // so K = Kp varies per expert.  The tiles are E x ceil(M / kBM) x ncol
-// (balanced row blocks), dealt to the XCDs in contiguous ranges; an expert
+// (row blocks of equal size), dealt to the XCDs in contiguous ranges; an expert
 // without rows writes zeros.  N is the row count of the dispatch, M passes
 // in `K`.
 template <int D, bool GATEUP, bool WG = false>

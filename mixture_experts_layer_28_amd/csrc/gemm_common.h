@@ -45,8 +45,9 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 // The tiles are (segment, row block, column block); only the segment sizes
 // on the device fix how many exist, so the grid is an upper bound.  A
 // segment of R rows has ceil(R / BM) row blocks: of BM rows each (the last
-// one shorter) or, with `balanced`, of floor or ceil of R / ceil(R / BM)
-// rows each, so that no row block is a thin remainder.  Pass 1 totals the
+// one shorter) or, with `balanced`, made of the ceil(R / 32) units of 32
+// rows (the last unit partial) dealt out as evenly as possible, so that no
+// row block is a thin remainder (BM a multiple of 32).  Pass 1 totals the
 // real tiles; they are then split evenly over the 8 XCDs (hardware deals
 // workgroup b to XCD b % 8; each XCD takes a contiguous range of logical
 // ids, so tiles that share operands share an L2), and pass 2 finds the
@@ -95,7 +96,13 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
         ti->col = (int)(rem / gs);
         const int64_t rb = first + rem % gs, R = hi - lo;
         if (balanced) {
-          const int64_t a = rb * R / nt, z = (rb + 1) * R / nt;
+          // whole 32-row units dealt out evenly (the last unit may be
+          // partial): a block's busiest SIMD carries ceil(rows / 32) of its
+          // 16-row MFMA tiles, so whole units leave no slot idle
+          const int64_t u = (R + 31) / 32;
+          const int64_t a = 32 * (rb * u / nt);
+          int64_t z = 32 * ((rb + 1) * u / nt);
+          z = z < R ? z : R;
           ti->row0 = lo + a;
           ti->rows = (int)(z - a);
         } else {
