@@ -79,6 +79,10 @@ def parse():
     p.add_argument("--clipped", action="store_true",
                    help="extension, not the benchmark: time the expert stage "
                         "with the plain and the clipped SwiGLU epilogue")
+    p.add_argument("--vendor-reference", action="store_true",
+                   help="extension, not the benchmark: the expert stage "
+                        "beside hipBLASLt (torch.mm) running the same "
+                        "per-expert GEMMs")
     p.add_argument("--cold-cache", action="store_true",
                    help="extension, not the benchmark: the forward with the "
                         "Infinity Cache flushed before every step; per-kernel "
@@ -486,6 +490,73 @@ def clipped_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def vendor_reference_bench(args):
+    """Extension, not the benchmark: the expert stage's two grouped GEMMs
+    beside the vendor library on the same work.  The reference runs, per
+    expert with rows, hipBLASLt (through torch.mm, bf16, FP32 accumulation)
+    on that expert's dispatched rows: xd_e . [W_gate; W_up]_e^T (one product
+    of 2I columns) and act_e . W_down_e^T, weights pre-transposed to
+    contiguous [K, N] outside the timed region; no SwiGLU (GEMMs only), so
+    the library's gate+up epilogue is extra work on its side.  Both run in
+    one process, alternating, torch events around each."""
+    import statistics
+    import torch
+
+    import mixture_experts_layer_28_amd as moe
+    from mixture_experts_layer_28_amd import workloads
+
+    base, T = WORKLOADS[args.workload]
+    wl = workloads.make(base, T=T, device="cuda")
+    idx, _ = moe.moe_route(wl["logits"], wl["k"], wl["renorm"])
+    d = moe.moe_dispatch(wl["x"], idx, wl["E"])
+    xd = d["xd"]
+    N, H, I, E = xd.shape[0], wl["H"], wl["I"], wl["E"]
+    off = d["offsets"].cpu().numpy().astype("int64")
+    segs = [(e, int(off[e]), int(off[e + 1])) for e in range(E)
+            if off[e + 1] > off[e]]
+    act = torch.empty((N, I), dtype=xd.dtype, device="cuda")
+    y = torch.empty((N, H), dtype=xd.dtype, device="cuda")
+    # [K, N] row-major copies of the weights for torch.mm (no transposed views)
+    wgu_t = [torch.cat([wl["w_gate"][e], wl["w_up"][e]], 0).t().contiguous()
+             for e, _, _ in segs]
+    wd_t = [wl["w_down"][e].t().contiguous() for e, _, _ in segs]
+    gu = torch.empty((N, 2 * I), dtype=xd.dtype, device="cuda")
+    yv = torch.empty((N, H), dtype=xd.dtype, device="cuda")
+
+    def vendor():
+        for (e, lo, hi), wg, wd in zip(segs, wgu_t, wd_t):
+            torch.mm(xd[lo:hi], wg, out=gu[lo:hi])
+            torch.mm(act[lo:hi], wd, out=yv[lo:hi])
+
+    calls = {
+        "library": lambda: moe.moe_experts_forward(
+            xd, d["offsets"], wl["w_gate"], wl["w_up"], wl["w_down"],
+            act=act, y=y),
+        "hipblaslt_per_expert": vendor,
+    }
+    times = {name: [] for name in calls}
+    for _ in range(args.warmup):
+        for call in calls.values():
+            call()
+    for _ in range(args.steps):
+        for name, call in calls.items():
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            times[name].append(a.elapsed_time(b))
+    flop = 6 * N * H * I
+    out = {"extension": "vendor_reference", "workload": base, "N": N,
+           "experts_with_rows": len(segs)}
+    for name, ts in times.items():
+        ms = statistics.median(ts)
+        out[name] = {"ms": round(ms, 4),
+                     "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    print(json.dumps(out), flush=True)
+
+
 def cold_cache_bench(args):
     """Extension, not the benchmark: the forward with the 256 MB Infinity
     Cache flushed before every step (a 1 GB fill, outside the events), so
@@ -727,6 +798,9 @@ def main():
         return
     if args.cold_cache:
         cold_cache_bench(args)
+        return
+    if args.vendor_reference:
+        vendor_reference_bench(args)
         return
     if args.copy_calibration:
         copy_calibration()
