@@ -6,8 +6,10 @@ One step = one moe_forward call (route -> dispatch -> SwiGLU experts ->
 combine) over one batch of synthetic inputs already resident in HBM; for the
 ``grouped`` workload, one moe_forward_sigmoid_grouped call (group-limited
 sigmoid routing in place of the softmax).  The default workload is the
-Mixtral-shaped bf16 layer (T=4096, H=4096, I=14336, E=8, top-2,
-renormalised).  W untimed steps, then K timed steps bracketed by
+largest single-GPU layer, the fine-grained many-expert bf16 layer (T=8192,
+H=7168, I=2048, E=64, top-8, renormalised, per-expert logit bias so some
+experts get no token); ``--workload mixtral``, ``decode32``, ``decode256``
+and ``grouped`` select the others.  W untimed steps, then K timed steps bracketed by
 device synchronisation; one JSON line on stdout.
 
 Per-kernel durations come from HIP events the library records around each of
@@ -28,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+METRIC = ("MoE forward tokens/sec + grouped-GEMM MFMA util; "
+          "route/dispatch/combine HBM GB/s")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -50,7 +54,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="mixtral", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="fine", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run one plain device copy of COPY_BYTES (for "
@@ -935,7 +939,7 @@ def main():
         cpu = cpu_baseline(wl)
 
     line = {
-        "metric": "MoE forward tokens/sec",
+        "metric": METRIC,
         "value": round(T * args.steps / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

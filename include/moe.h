@@ -36,6 +36,11 @@
  * - Element types: moe_dtype.  Activations, expert weights and expert
  *   outputs share one dtype `dt`; logits and routing weights share `ldt`
  *   (the guide admits F32, F16 and BF16 for both).
+ * - Where a declaration below says "No passage of the pages", the call is
+ *   this library's own (host arithmetic or instrumentation) and the pages
+ *   define nothing it computes.  Size limits beyond those the guide states
+ *   (the E limits of routing, dispatch and the experts, top_k <= 8192 in
+ *   combine) are this library's, not the pages'.
  */
 #ifndef MOE_MI355X_MOE_H
 #define MOE_MI355X_MOE_H
@@ -86,7 +91,8 @@ typedef enum moe_status {
  * selected probabilities are divided by their FP32 sum.  The weights are
  * then rounded (nearest even) to ldt.  A row holding a NaN, a +inf, or only
  * -inf gets weights NaN and indices 0..top_k-1.
- * Requires 1 <= top_k <= E.  E <= 65536.
+ * Requires 1 <= top_k <= E (guide, section 4).  E <= 65536 is this
+ * library's limit, not the pages' (MOE_ERR_UNSUPPORTED beyond).
  */
 int moe_route(const void* logits, int ldt, int64_t T, int64_t E,
               int64_t top_k, int renormalize, uint32_t* idx, void* weights,
@@ -94,7 +100,9 @@ int moe_route(const void* logits, int ldt, int64_t T, int64_t E,
 
 /*
  * moe_dispatch_workspace_size - bytes of scratch moe_dispatch needs for
- * (T, E, top_k).  Pure host arithmetic; returns 0 for invalid sizes.
+ * (T, E, top_k): the per-chunk expert count table.  No passage of the
+ * pages: pure host arithmetic of this library's dispatch layout; never
+ * touches the device.  Returns 0 for invalid sizes.
  */
 size_t moe_dispatch_workspace_size(int64_t T, int64_t E, int64_t top_k);
 
@@ -120,6 +128,8 @@ size_t moe_dispatch_workspace_size(int64_t T, int64_t E, int64_t top_k);
  * its rows are placed after offsets[E] with row_expert 0xFFFFFFFF (so
  * offsets[E] < N signals it), every access stays in bounds, and
  * moe_experts_forward writes zeros for those rows.
+ * E <= 16383 is this library's limit, not the pages' (the per-chunk count
+ * table must fit in LDS; MOE_ERR_UNSUPPORTED beyond).
  */
 int moe_dispatch(const void* x, int dt, int64_t T, int64_t H, int64_t E,
                  int64_t top_k, const uint32_t* idx, void* xd,
@@ -143,7 +153,8 @@ int moe_dispatch(const void* x, int dt, int64_t T, int64_t H, int64_t E,
  * (FP32 accumulation, each rounded to dt), act = SiLU(g) * u (FP32, rounded
  * to dt), y[r] = act . w_down[e]^T (FP32 accumulation, rounded to dt).
  * Segments must be monotone with offsets[0] == 0 and offsets[E] <= N; rows
- * in [offsets[E], N) get y = 0.
+ * in [offsets[E], N) get y = 0 and their act rows are not written.
+ * E <= 16383 is this library's limit, not the pages'.
  */
 int moe_experts_forward(const void* xd, int dt, int64_t N, int64_t H,
                         int64_t I, int64_t E, const void* w_gate,
@@ -186,8 +197,10 @@ int moe_combine(const void* y, int dt, int64_t N, int64_t T, int64_t H,
                 const uint32_t* token_row, void* out, void* stream);
 
 /*
- * moe_forward_workspace_size - bytes of scratch moe_forward needs.
- * Returns 0 for invalid arguments.
+ * moe_forward_workspace_size - bytes of scratch moe_forward needs.  No
+ * passage of the pages: pure host arithmetic of this library's workspace
+ * layout (routing result, dispatch mapping and rows, count table, act, y);
+ * never touches the device.  Returns 0 for invalid arguments.
  */
 size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E,
                                   int64_t top_k, int dt, int ldt);
@@ -203,8 +216,8 @@ size_t moe_forward_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E,
  *   out    [T,H]   dt    output
  *   workspace  moe_forward_workspace_size(...) bytes, 256-byte aligned
  *
- * Limits are those of the four stages: 1 <= top_k <= E, E <= 16383,
- * top_k <= 8192, T*top_k < 2^32.  The workspace holds the routing result,
+ * Limits are those of the four stages: 1 <= top_k <= E (guide, section 4);
+ * E <= 16383, top_k <= 8192 and T*top_k < 2^32 are this library's.  The workspace holds the routing result,
  * the dispatch mapping and rows, the dispatch count table, act and y.
  */
 int moe_forward(const void* x, int dt, const void* logits, int ldt,
@@ -215,8 +228,9 @@ int moe_forward(const void* x, int dt, const void* logits, int ldt,
 
 /*
  * moe_forward_clipped - moe_forward with the clipped SwiGLU activation of
- * moe_experts_forward_clipped (alpha finite, limit finite and >= 0,
- * MOE_ERR_INVALID_ARG otherwise).  Workspace and limits as moe_forward.
+ * moe_experts_forward_clipped (MindSpeed-Ops page, clipped_swiglu parameter
+ * table; alpha finite, limit finite and >= 0, MOE_ERR_INVALID_ARG
+ * otherwise).  Workspace and limits as moe_forward.
  */
 int moe_forward_clipped(const void* x, int dt, const void* logits, int ldt,
                         int64_t T, int64_t H, int64_t I, int64_t E,
@@ -399,7 +413,8 @@ int moe_combine_backward(const void* y, int dt, int64_t N, int64_t T,
  * moe_experts_backward_workspace_size - bytes of scratch
  * moe_experts_backward needs (one transposed weight tensor, three [N,I] and
  * two [N,H] intermediates, two [N+8*E,max(H,I)] transposed operand
- * copies).
+ * copies).  No passage of the pages: pure host arithmetic of this
+ * library's workspace layout; never touches the device.
  * Returns 0 for invalid arguments.
  */
 size_t moe_experts_backward_workspace_size(int64_t N, int64_t H, int64_t I,
@@ -461,7 +476,9 @@ int moe_dispatch_backward(const void* grad_xd, int dt, int64_t N, int64_t T,
                           void* stream);
 
 /*
- * moe_set_timing_events - instrumentation for measuring each kernel.
+ * moe_set_timing_events - instrumentation for measuring each kernel.  No
+ * passage of the pages: this library's own timing hook; it changes no
+ * result.
  *
  * events: `count` hipEvent_t handles created by the caller (hipEventCreate),
  * or NULL with count 0 to switch recording off.  While set, every
@@ -478,10 +495,23 @@ int moe_dispatch_backward(const void* grad_xd, int dt, int64_t N, int64_t T,
 #define MOE_TIMING_EVENTS 8
 int moe_set_timing_events(void* const* events, int count);
 
-/* Static text for a status code. */
+/*
+ * moe_status_string - static text for a status code ("unknown status" for
+ * codes outside moe_status).  The status codes stand for the pages'
+ * MoeError results: the guide's MoE calls return a Result with MoeError
+ * (guide, section 3 "MoE workflow" and section 6 "calling MoE"), and the
+ * experts page's SwiGluExperts::new and forward_dispatched_with_strategy
+ * reject mismatched ranks, shapes and dtypes with static messages.
+ */
 const char* moe_status_string(int status);
 
-/* Detail of the last failed call on this thread ("" if none). */
+/*
+ * moe_last_error - detail of the last failed call on this thread ("" if
+ * the last call succeeded): the static-message text of the pages' MoeError
+ * (guide, sections 3 and 6; experts page, SwiGluExperts::new), plus the
+ * offending values.  The string stays valid until the next call on this
+ * thread.
+ */
 const char* moe_last_error(void);
 
 #ifdef __cplusplus

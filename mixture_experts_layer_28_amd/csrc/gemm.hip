@@ -432,9 +432,11 @@ hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
   if (N < 96 * (int64_t)E)
     return launch_mfma_pair<D, 32, 128, 1, MOE_DECODE_NT>(xd, N, H, I, E, wg, wu, wd,
                                            offsets, act, y, st, sw);
-  // Prefill: 256 x 256 tiles when every buffer range fits 31 bits.
+  // Prefill: row blocks of up to 320 rows x 256 columns when every buffer
+  // range fits 31 bits (the K-tail loads use offset 2^31 as "past the end",
+  // so a row block's A range, 320 rows of K elements, must stay below it).
   const int64_t lim = (int64_t)1 << 31;
-  if (H * I * 2 < lim && 256 * H * 2 < lim && 256 * I * 2 < lim) {
+  if (H * I * 2 < lim && 320 * H * 2 < lim && 320 * I * 2 < lim) {
     return launch_experts_big(xd, D, N, H, I, E, wg, wu, wd, offsets, act, y,
                               st, sw);
   }
@@ -460,7 +462,7 @@ hipError_t launch_nt_mfma(const void* A, int64_t N, int64_t K, const void* B,
     return hipGetLastError();
   }
   const int64_t lim = (int64_t)1 << 31;
-  if (K * NB * 2 < lim && 256 * K * 2 < lim && 256 * NB * 2 < lim)
+  if (K * NB * 2 < lim && 320 * K * 2 < lim && 320 * NB * 2 < lim)
     return launch_nt_big(A, D, N, (int)K, B, (int)NB, E, offsets, C, st);
   const uint32_t ncol = cdiv(NB, 128);
   const uint32_t grid = tile_grid(ncol * (cdiv(N, 128) + (uint32_t)nseg));

@@ -184,20 +184,31 @@ def expert_rows(xd, e, w_gate, w_up, w_down, fmt, clip=None):
     product is an exact float64 matrix product rounded once; gate, up and act
     are rounded to ``fmt`` as the experts page stores them (R-Prec).
     """
+    return round_to(expert_act(xd, w_gate, w_up, fmt, clip) @ w_down.T, fmt)
+
+
+def expert_act(xd, w_gate, w_up, fmt, clip=None):
+    """The activation rows of one expert, act = SwiGLU(gate, up) [n,I]: the
+    gate and up products (exact float64 sums rounded once to ``fmt``), then
+    SiLU(gate) * up (or the clipped form) rounded to ``fmt`` ([Experts]
+    forward_dispatched_with_strategy stores gate, up and this result as
+    tensors of the weight dtype; R-Prec)."""
     g = round_to(xd @ w_gate.T, fmt)
     u = round_to(xd @ w_up.T, fmt)
-    a = round_to(silu_times(g, u) if clip is None
-                 else clipped_silu_times(g, u, *clip), fmt)
-    return round_to(a @ w_down.T, fmt)
+    return round_to(silu_times(g, u) if clip is None
+                    else clipped_silu_times(g, u, *clip), fmt)
 
 
-def experts(xd, offsets, w_gate, w_up, w_down, fmt, rows=None, clip=None):
+def experts(xd, offsets, w_gate, w_up, w_down, fmt, rows=None, clip=None,
+            with_act=False):
     """Grouped SwiGLU over expert segments.
 
     xd [N,H], offsets [E+1]; weights in ``fmt`` (decoded here).  If ``rows``
     is given, only those dispatched rows are computed (returned in that
     order); otherwise all N rows.  ``clip`` = (alpha, limit) selects the
-    clipped SwiGLU activation.
+    clipped SwiGLU activation.  With ``with_act`` the activation rows
+    [len(rows), I] are returned too, as (y, act); rows of no expert give
+    zeros in both.
     """
     xd = decode(xd, fmt)
     E = len(offsets) - 1
@@ -205,6 +216,7 @@ def experts(xd, offsets, w_gate, w_up, w_down, fmt, rows=None, clip=None):
     I = np.asarray(w_gate).shape[1]
     want = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.zeros((len(want), H), dtype=np.float64)
+    act = np.zeros((len(want), I), dtype=np.float64)
     seg = np.searchsorted(np.asarray(offsets), want, side="right") - 1
     for e in range(E):
         sel = np.nonzero(seg == e)[0]
@@ -214,8 +226,10 @@ def experts(xd, offsets, w_gate, w_up, w_down, fmt, rows=None, clip=None):
         wu = decode(np.asarray(w_up)[e], fmt)
         wd = decode(np.asarray(w_down)[e], fmt)
         assert wg.shape == (I, H) and wd.shape == (H, I)
-        out[sel] = expert_rows(xd[want[sel]], e, wg, wu, wd, fmt, clip)
-    return out
+        a = expert_act(xd[want[sel]], wg, wu, fmt, clip)
+        act[sel] = a
+        out[sel] = round_to(a @ wd.T, fmt)
+    return (out, act) if with_act else out
 
 
 # ---------------------------------------------------------------------------

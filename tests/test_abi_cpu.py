@@ -365,3 +365,26 @@ def test_forward_clipped_rejects():
     a = list(args)
     a[4] = 0
     assert L.moe_forward_clipped(*a) == 0
+
+
+CITES = ("guide, section", "guide, sections", "experts page",
+         "MindSpeed-Ops page", "No passage of the pages")
+
+
+def test_every_declaration_cites_a_passage_or_says_it_has_none():
+    """Each exported declaration's own comment names the passage of the
+    pages that defines it (the ruDNN user guide's sections, the experts
+    page, the MindSpeed-Ops page), or states that none does (host
+    arithmetic and instrumentation)."""
+    src = open(HEADER).read()
+    decls = re.finditer(
+        r"/\*((?:(?!\*/).)*)\*/\s*(?:#define[^\n]*\n\s*)?"
+        r"(?:int|size_t|const char\*)\s+(moe_[a-z_]+)\s*\(", src, flags=re.S)
+    seen = {}
+    for m in decls:
+        text = " ".join(m.group(1).replace("*", " ").split())
+        seen[m.group(2)] = text
+    assert sorted(seen) == _declared()
+    for name, text in seen.items():
+        assert text.startswith(name) or name in text, name
+        assert any(c in text for c in CITES), name

@@ -52,12 +52,27 @@ def _case(rng, T, H, I, E, k, fmt, skew=False, std=None):
 
 
 def _experts_gpu(d, wg, wu, wd, fmt):
+    """GPU expert stage on the oracle's dispatch: (y, act) as float64
+    values.  act is the fused gate+up kernel's own output, SiLU(gate)*up."""
+    N, I = len(d["xd"]), np.asarray(wg).shape[1]
+    act = torch.empty((N, I), dtype=TDT[fmt], device="cuda")
     y = moe.moe_experts_forward(
         _tensor(d["xd"], fmt).cuda(), _u32(d["offsets"]).cuda(),
         _tensor(wg, fmt).cuda(), _tensor(wu, fmt).cuda(),
-        _tensor(wd, fmt).cuda())
+        _tensor(wd, fmt).cuda(), act=act)
     torch.cuda.synchronize()
-    return values(y)
+    return values(y), values(act)
+
+
+def _check_stage(d, wg, wu, wd, fmt, what):
+    """Both outputs of the expert stage against the oracle, elementwise:
+    act (the gate+up kernel's SwiGLU rows) and y (the down product)."""
+    y_ref, act_ref = experts(d["xd"], d["offsets"], wg, wu, wd, fmt,
+                             with_act=True)
+    y_gpu, act_gpu = _experts_gpu(d, wg, wu, wd, fmt)
+    assert_close(act_gpu, act_ref, fmt, "act: " + what)
+    assert_close(y_gpu, y_ref, fmt, "y: " + what)
+    return y_gpu, act_gpu
 
 
 # (T, H, I, E, k, fmt, skew): several tiles, ragged row/column/K tails,
@@ -83,9 +98,7 @@ SHAPES = [
 def test_experts_stage(T, H, I, E, k, fmt, skew):
     rng = np.random.default_rng(T * 7 + H + I + E)
     x, lg, wg, wu, wd, idx, w, d = _case(rng, T, H, I, E, k, fmt, skew)
-    y_ref = experts(d["xd"], d["offsets"], wg, wu, wd, fmt)
-    y_gpu = _experts_gpu(d, wg, wu, wd, fmt)
-    assert_close(y_gpu, y_ref, fmt, "experts %s" % ((T, H, I, E, k, fmt),))
+    _check_stage(d, wg, wu, wd, fmt, "experts %s" % ((T, H, I, E, k, fmt),))
 
 
 @pytest.mark.parametrize("R", [321, 639, 641, 1035, 1065, 1281])
@@ -107,9 +120,7 @@ def test_balanced_row_blocks(R):
     idx = idx[rng.permutation(T)]
     d = dispatch(x, idx, E)
     assert d["offsets"][1] == R
-    y_ref = experts(d["xd"], d["offsets"], wg, wu, wd, fmt)
-    y_gpu = _experts_gpu(d, wg, wu, wd, fmt)
-    assert_close(y_gpu, y_ref, fmt, "balanced blocks R=%d" % R)
+    _check_stage(d, wg, wu, wd, fmt, "balanced blocks R=%d" % R)
 
 
 @pytest.mark.parametrize("H,I,fmt", [(40, 48, "bf16"), (104, 72, "bf16"),
@@ -132,9 +143,7 @@ def test_short_segments_in_prefill_tiles(H, I, fmt):
     idx = idx[rng.permutation(T)]
     d = dispatch(x, idx, E)
     assert list(np.diff(d["offsets"])) == sizes
-    y_ref = experts(d["xd"], d["offsets"], wg, wu, wd, fmt)
-    y_gpu = _experts_gpu(d, wg, wu, wd, fmt)
-    assert_close(y_gpu, y_ref, fmt, "short segments H=%d I=%d" % (H, I))
+    _check_stage(d, wg, wu, wd, fmt, "short segments H=%d I=%d" % (H, I))
 
 
 def test_largest_expert_count():
@@ -149,9 +158,7 @@ def test_largest_expert_count():
     wu = round_to(rng.standard_normal((E, I, H)) / 4.0, fmt)
     wd = round_to(rng.standard_normal((E, H, I)) / 5.0, fmt)
     d = dispatch(x, idx, E)
-    y_ref = experts(d["xd"], d["offsets"], wg, wu, wd, fmt)
-    y_gpu = _experts_gpu(d, wg, wu, wd, fmt)
-    assert_close(y_gpu, y_ref, fmt, "E=16383")
+    _check_stage(d, wg, wu, wd, fmt, "E=16383")
 
 
 def test_experts_zero_rows_for_trailing_segment():
@@ -161,9 +168,11 @@ def test_experts_zero_rows_for_trailing_segment():
     off = d["offsets"].copy()
     off[4] = 70  # rows 70..79 lie past the last segment
     d2 = dict(d, offsets=off)
-    y = _experts_gpu(d2, wg, wu, wd, fmt)
-    assert np.all(y[70:] == 0.0)
-    y_ref = experts(d["xd"][:70], off, wg, wu, wd, fmt)
+    y, act = _experts_gpu(d2, wg, wu, wd, fmt)
+    assert np.all(y[70:] == 0.0)  # act rows of no expert are not written
+    y_ref, act_ref = experts(d["xd"][:70], off, wg, wu, wd, fmt,
+                             with_act=True)
+    assert_close(act[:70], act_ref, fmt, "head rows (act)")
     assert_close(y[:70], y_ref, fmt, "head rows")
 
 
@@ -201,35 +210,77 @@ def test_combine_k1_weight_one_is_exact():
     np.testing.assert_array_equal(values(out), y[tr[:, 0]])
 
 
-@pytest.mark.parametrize("name,T,nrows", [("mixtral", 4096, 24),
-                                          ("fine", 8192, 48),
-                                          ("decode", 32, 64),
-                                          ("decode", 256, 64)])
-def test_experts_full_size_sampled(name, T, nrows):
-    """Full-size expert stage (the launch configuration of the benchmark)
-    checked on sampled dispatched rows; the oracle computes those rows one
-    by one from the workload's inputs."""
+def unit_boundary_rows(offsets, N, unit=32):
+    """The first and last row of every 32-row unit of every segment.  Every
+    row block of both expert kernels is made of whole 32-row units of one
+    segment (the prefill kernel's blocks of up to 320 rows, the decode
+    kernel's 32-row tiles), so these rows include the first and the last
+    row of every (expert, row block) tile."""
+    rows = []
+    off = np.asarray(offsets, dtype=np.int64)
+    for e in range(len(off) - 1):
+        lo, hi = int(min(off[e], N)), int(min(off[e + 1], N))
+        for a in range(lo, hi, unit):
+            rows += [a, min(a + unit, hi) - 1]
+    return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def test_unit_boundary_rows_cover_every_tile():
+    off = np.array([0, 0, 1, 33, 33, 353, 1000])
+    rows = unit_boundary_rows(off, 1000)
+    for lo, hi in zip(off[:-1], off[1:]):
+        if hi > lo:
+            assert lo in rows and hi - 1 in rows
+            for a in range(lo, hi, 32):
+                assert a in rows and min(a + 32, hi) - 1 in rows
+    assert rows.max() == 999
+
+
+@pytest.mark.parametrize("name,T,every_row", [("mixtral", 4096, True),
+                                              ("fine", 8192, False),
+                                              ("decode", 32, True),
+                                              ("decode", 256, True)])
+def test_experts_full_size(name, T, every_row):
+    """Full-size expert stage in the launch configuration of the benchmark:
+    both outputs (act, the fused gate+up kernel's SiLU(gate)*up, and y, the
+    down product) compared elementwise over whole rows with the float64
+    oracle.  Mixtral and decode: every dispatched row.  Fine (65536 rows):
+    the first and last row of every 32-row unit of every segment (so of
+    every tile of the tile map, whatever its column block: whole rows are
+    compared) plus 256 random rows."""
     wl = workloads.make(name, T=T, device="cuda")
     E, k, fmt = wl["E"], wl["k"], wl["fmt"]
+    I = wl["I"]
     idx, _ = route(values(wl["logits"]), k, wl["renorm"], fmt)
     d = dispatch(np.zeros((T, 1)), idx, E)
-    xd = wl["x"][torch.from_numpy(d["row_token"].astype(np.int64)).cuda()]
-    y = moe.moe_experts_forward(xd, _u32(d["offsets"]).cuda(), wl["w_gate"],
-                                wl["w_up"], wl["w_down"])
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
     N = T * k
-    rows = np.unique(np.concatenate([
-        rng.choice(N, size=nrows, replace=False),
-        d["offsets"][1:-1][d["offsets"][1:-1] < N],   # segment starts
-        np.maximum(d["offsets"][1:] - 1, 0)]))[:3 * nrows]  # segment ends
+    xd = wl["x"][torch.from_numpy(d["row_token"].astype(np.int64)).cuda()]
+    act = torch.empty((N, I), dtype=wl["x"].dtype, device="cuda")
+    y = moe.moe_experts_forward(xd, _u32(d["offsets"]).cuda(), wl["w_gate"],
+                                wl["w_up"], wl["w_down"], act=act)
+    torch.cuda.synchronize()
+    if every_row:
+        rows = np.arange(N)
+    else:
+        rng = np.random.default_rng(0)
+        rows = np.unique(np.concatenate([
+            unit_boundary_rows(d["offsets"], N),
+            rng.choice(N, size=256, replace=False)]))
+    # every non-empty segment contributes its first and last row
+    seg = np.searchsorted(d["offsets"], rows, side="right") - 1
+    for e in range(E):
+        lo, hi = d["offsets"][e], d["offsets"][e + 1]
+        if hi > lo:
+            assert lo in rows and hi - 1 in rows, e
     gw = {key: workloads.to_numpy(wl[key], fmt)
           for key in ("w_gate", "w_up", "w_down")}
     xd_np = workloads.to_numpy(wl["x"], fmt)[d["row_token"][rows]]
     # oracle on just these rows: a dispatched view holding them in order
-    seg = np.searchsorted(d["offsets"], rows, side="right") - 1
     sub_off = np.searchsorted(seg, np.arange(E + 1), side="left")
-    y_ref = experts(xd_np, sub_off, gw["w_gate"], gw["w_up"], gw["w_down"],
-                    fmt)
-    assert_close(values(y[torch.from_numpy(rows).cuda()]), y_ref, fmt,
-                 "%s sampled rows" % name)
+    y_ref, act_ref = experts(xd_np, sub_off, gw["w_gate"], gw["w_up"],
+                             gw["w_down"], fmt, with_act=True)
+    sel = torch.from_numpy(rows).cuda()
+    assert_close(values(act[sel]), act_ref, fmt,
+                 "%s T=%d act, %d rows" % (name, T, len(rows)))
+    assert_close(values(y[sel]), y_ref, fmt,
+                 "%s T=%d y, %d rows" % (name, T, len(rows)))

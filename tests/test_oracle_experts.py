@@ -14,7 +14,14 @@ Pins (none reuses the oracle's vectorised code):
 * H = I = 1 scalar closed form;
 * k = 1 with renormalisation: the output is the expert row, bit for bit;
 * identical experts with renormalisation: the output does not depend on
-  the routing (the weights sum to one).
+  the routing (the weights sum to one);
+* the activation rows (``experts(..., with_act=True)``) equal the loops'
+  SiLU(gate) * up bit for bit, every format;
+* the token-by-token forward (``forward_tokens``, the checker behind the
+  full-size end-to-end tests) equals the loops directly, and the full
+  forward restricted to its tokens bit for bit, for every format, k in
+  {1, 2, E}, both renormalisation settings, poisoned rows and unsorted,
+  repeated token lists.
 """
 
 import itertools
@@ -25,16 +32,18 @@ import pytest
 import torch
 
 from oracle.fp import round_to
-from oracle.moe import combine, dispatch, experts, forward, route
+from oracle.moe import (combine, dispatch, experts, forward, forward_tokens,
+                        route)
 
 
 def _rnd(v, fmt):
     return float(round_to(np.array([v]), fmt)[0])
 
 
-def _mlp_loops(x, wg, wu, wd, fmt):
+def _mlp_loops(x, wg, wu, wd, fmt, with_act=False):
     """One token through one expert with explicit loops.
-    wg, wu: nested lists [I][H]; wd: [H][I]."""
+    wg, wu: nested lists [I][H]; wd: [H][I].  With ``with_act`` also the
+    activation row a (the experts page's stored SwiGLU result)."""
     H, I = len(x), len(wg)
     g = [_rnd(math.fsum(x[h] * wg[i][h] for h in range(H)), fmt)
          for i in range(I)]
@@ -47,8 +56,9 @@ def _mlp_loops(x, wg, wu, wd, fmt):
         except OverflowError:
             sig = 0.0
         a.append(_rnd(g[i] * sig * u[i], fmt))
-    return [_rnd(math.fsum(a[i] * wd[h][i] for i in range(I)), fmt)
-            for h in range(H)]
+    y = [_rnd(math.fsum(a[i] * wd[h][i] for i in range(I)), fmt)
+         for h in range(H)]
+    return (y, a) if with_act else y
 
 
 def _case(rng, T, H, I, E, fmt):
@@ -162,3 +172,80 @@ def test_poisoned_row_gives_nan_output_only_there():
     bad = np.isnan(res["out"]).all(axis=1)
     assert bad.tolist() == [False, False, True, False, True, False]
     assert not np.isnan(res["out"][~bad]).any()
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_activation_rows_brute_force(fmt):
+    rng = np.random.default_rng({"f32": 31, "f16": 32, "bf16": 33}[fmt])
+    T, H, I, E, k = 6, 3, 5, 3, 2
+    x, lg, wg, wu, wd = _case(rng, T, H, I, E, fmt)
+    idx, _ = route(lg, k, True, fmt)
+    d = dispatch(x, idx, E)
+    y, act = experts(d["xd"], d["offsets"], wg, wu, wd, fmt, with_act=True)
+    assert act.shape == (T * k, I)
+    for r in range(T * k):
+        e = int(d["row_expert"][r])
+        yl, al = _mlp_loops(list(d["xd"][r]), wg[e].tolist(), wu[e].tolist(),
+                            wd[e].tolist(), fmt, with_act=True)
+        assert act[r].tolist() == al, (fmt, r)
+        assert y[r].tolist() == yl, (fmt, r)
+    # a row subset returns the same activation rows, in the order asked
+    rows = [7, 0, 11, 3]
+    ys, acts = experts(d["xd"], d["offsets"], wg, wu, wd, fmt, rows=rows,
+                       with_act=True)
+    np.testing.assert_array_equal(acts, act[rows])
+    np.testing.assert_array_equal(ys, y[rows])
+
+
+def _poison(lg):
+    lg = lg.copy()
+    lg[1, 0] = np.nan
+    lg[3, 2] = np.inf
+    lg[4] = -np.inf
+    return lg
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_forward_tokens_brute_force(fmt):
+    """forward_tokens against explicit loops: route, each slot's expert on
+    the token row, the weighted sum in slot order rounded once."""
+    rng = np.random.default_rng({"f32": 41, "f16": 42, "bf16": 43}[fmt])
+    T, H, I, E = 6, 3, 5, 4
+    x, lg, wg, wu, wd = _case(rng, T, H, I, E, fmt)
+    lg = _poison(lg)
+    tokens = [5, 0, 3, 3, 1, 4]
+    for k, renorm in itertools.product((1, 2, E), (False, True)):
+        idx, w, out = forward_tokens(x, lg, wg, wu, wd, k, renorm, fmt,
+                                     tokens)
+        ridx, rw = route(lg[tokens], k, renorm, fmt)
+        np.testing.assert_array_equal(idx, ridx)
+        np.testing.assert_array_equal(w, rw)
+        for n, t in enumerate(tokens):
+            acc = []
+            for j in range(k):
+                e = int(idx[n, j])
+                y = _mlp_loops(list(x[t]), wg[e].tolist(), wu[e].tolist(),
+                               wd[e].tolist(), fmt)
+                acc.append([w[n, j] * v for v in y])
+            if np.isnan(w[n]).any():
+                assert np.isnan(out[n]).all(), (k, renorm, t)
+                continue
+            want = [_rnd(math.fsum(col), fmt) for col in zip(*acc)]
+            assert out[n].tolist() == want, (fmt, k, renorm, t)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_forward_tokens_equals_full_forward(fmt):
+    rng = np.random.default_rng({"f32": 51, "f16": 52, "bf16": 53}[fmt])
+    T, H, I, E = 9, 8, 12, 5
+    x, lg, wg, wu, wd = _case(rng, T, H, I, E, fmt)
+    lg = _poison(lg)
+    tokens = [8, 2, 2, 0, 4, 1, 3, 7]   # unsorted, one repeated
+    for k, renorm in itertools.product((1, 2, E), (False, True)):
+        full = forward(x, lg, wg, wu, wd, k, renorm, fmt)
+        idx, w, out = forward_tokens(x, lg, wg, wu, wd, k, renorm, fmt,
+                                     tokens)
+        np.testing.assert_array_equal(idx, full["idx"][tokens])
+        np.testing.assert_array_equal(w, full["w"][tokens])
+        np.testing.assert_array_equal(out, full["out"][tokens])
+        assert np.isnan(out[[tokens.index(t) for t in (1, 3, 4)]]).all()
