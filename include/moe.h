@@ -138,6 +138,26 @@ int moe_dispatch(const void* x, int dt, int64_t T, int64_t H, int64_t E,
                  void* stream);
 
 /*
+ * moe_dispatch_noalloc - moe_dispatch for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments, outputs and
+ * results without the workspace.  The count table lives in a static
+ * device array of 4 MiB (2^20 uint32 entries) that each device the
+ * library runs on holds until the process ends; no call allocates or frees
+ * anything.  Sizes whose table would need more than that (very large E
+ * times many chunks; never below E = 16383 with T*top_k <= 2^26) return
+ * MOE_ERR_UNSUPPORTED before anything is enqueued.  All calls on one device
+ * share the array, so calls that overlap on one device (concurrent
+ * streams, or threads) race: serialise them.  Every table entry a call
+ * reads is written by that call first, so nothing needs clearing.
+ */
+int moe_dispatch_noalloc(const void* x, int dt, int64_t T, int64_t H,
+                         int64_t E, int64_t top_k, const uint32_t* idx,
+                         void* xd, uint32_t* offsets, uint32_t* row_expert,
+                         uint32_t* row_token, uint32_t* token_row,
+                         void* stream);
+
+/*
  * moe_experts_forward - SwiGLU experts over expert segments (experts page,
  * forward_dispatched_with_strategy; weight layouts from SwiGluExperts::new).
  *

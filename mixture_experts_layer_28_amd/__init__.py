@@ -9,7 +9,8 @@ only marshal arguments.
 """
 
 from .ops import (moe_combine, moe_combine_backward, moe_dispatch,
-                  moe_dispatch_backward, moe_dispatch_workspace_size,
+                  moe_dispatch_backward, moe_dispatch_noalloc,
+                  moe_dispatch_workspace_size,
                   moe_experts_backward, moe_experts_backward_workspace_size,
                   moe_experts_forward, moe_experts_forward_clipped,
                   moe_experts_forward_training,
@@ -26,4 +27,5 @@ __all__ = ["moe_route", "moe_dispatch", "moe_dispatch_workspace_size",
            "moe_selected_router_backward", "moe_experts_forward_training",
            "moe_combine_backward", "moe_experts_backward_workspace_size",
            "moe_experts_backward", "moe_dispatch_backward",
-           "moe_experts_forward_clipped", "moe_forward_clipped"]
+           "moe_experts_forward_clipped", "moe_forward_clipped",
+           "moe_dispatch_noalloc"]

@@ -27,6 +27,8 @@ SIGNATURES = {
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "moe_dispatch": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P, _P,
                             _P, _P, _P, _P, _SZ, _P]),
+    "moe_dispatch_noalloc": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P,
+                                    _P, _P, _P, _P, _P, _P]),
     "moe_experts_forward": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P,
                                    _P, _P, _P, _P, _P]),
     "moe_experts_forward_clipped": (_INT, [_P, _INT, _I64, _I64, _I64, _I64,

@@ -22,10 +22,21 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <atomic>
+
 namespace moe {
 namespace {
 
 constexpr int kMaxTable = 1 << 20;  // u32 entries of the count table
+
+// The count table of moe_dispatch_noalloc, for callers that cannot
+// allocate: kMaxTable u32 entries (4 MiB) held by every device the library
+// runs on until the process ends.  Host code never passes this name to a
+// kernel (on the host it is only a stand-in for the symbol): it passes the
+// per-device address from dispatch_scratch().  The count kernel writes
+// every table entry a call reads, so nothing needs clearing between calls;
+// calls that overlap on one device share the table and race.
+static __device__ __align__(256) uint32_t scratch[kMaxTable];
 
 __global__ void dispatch_count_kernel(const uint32_t* __restrict__ idx,
                                       int64_t N, int E, int64_t chunk,
@@ -261,6 +272,27 @@ DispatchPlan plan_dispatch(int64_t T, int64_t E, int64_t k) {
   p.waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
   p.table_bytes = (size_t)(p.nchunks * (E + 1)) * sizeof(uint32_t);
   return p;
+}
+
+size_t dispatch_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t dispatch_scratch(void** ptr) {
+  // device address of `scratch` on the current device, looked up once per
+  // device id below 64 (each device holds its own copy at its own address)
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const bool cached = dev >= 0 && dev < 64;
+  void* p = cached ? addr[dev].load(std::memory_order_acquire) : nullptr;
+  if (!p) {
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    if (cached) addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,

@@ -67,6 +67,11 @@ hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,
                            uint32_t* row_token, uint32_t* token_row,
                            void* workspace, const DispatchPlan& plan,
                            hipStream_t st);
+// The static count table of moe_dispatch_noalloc: its size, and its device
+// address on the current device (looked up once per device, never
+// allocated).
+size_t dispatch_scratch_bytes();
+hipError_t dispatch_scratch(void** ptr);
 
 // ---- experts ---------------------------------------------------------------
 // Activation of the gate+up epilogue: limit < 0 is the plain SiLU(g) * u;

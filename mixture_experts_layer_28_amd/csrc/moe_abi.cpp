@@ -366,6 +366,31 @@ int moe_dispatch(const void* x, int dt, int64_t T, int64_t H, int64_t E,
       "moe_dispatch");
 }
 
+int moe_dispatch_noalloc(const void* x, int dt, int64_t T, int64_t H,
+                         int64_t E, int64_t top_k, const uint32_t* idx,
+                         void* xd, uint32_t* offsets, uint32_t* row_expert,
+                         uint32_t* row_token, uint32_t* token_row,
+                         void* stream) {
+  int s = check_dispatch(x, dt, T, H, E, top_k, idx, xd, offsets, row_expert,
+                         row_token, token_row);
+  if (s != MOE_OK) return s;
+  const moe::DispatchPlan plan = moe::plan_dispatch(T, E, top_k);
+  const size_t cap = moe::dispatch_scratch_bytes();
+  if (plan.table_bytes > cap)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_dispatch_noalloc: the count table needs %zu bytes, more "
+                "than the %zu-byte static scratch (use moe_dispatch)",
+                plan.table_bytes, cap);
+  void* table = nullptr;
+  hipError_t err = moe::dispatch_scratch(&table);
+  if (err != hipSuccess) return hip_status(err, "moe_dispatch_noalloc");
+  return hip_status(
+      moe::launch_dispatch(x, dt, T, H, (int)E, (int)top_k, idx, xd, offsets,
+                           row_expert, row_token, token_row, table, plan,
+                           (hipStream_t)stream),
+      "moe_dispatch_noalloc");
+}
+
 int moe_experts_forward(const void* xd, int dt, int64_t N, int64_t H,
                         int64_t I, int64_t E, const void* w_gate,
                         const void* w_up, const void* w_down,

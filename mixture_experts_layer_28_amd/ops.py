@@ -134,6 +134,31 @@ def moe_dispatch(x, idx, num_experts, workspace=None):
     return out
 
 
+def moe_dispatch_noalloc(x, idx, num_experts, out=None):
+    """moe_dispatch without a workspace (the library's static count table).
+    ``out``: optional dict of caller-allocated outputs with the keys of
+    moe_dispatch's result (then this call allocates nothing); missing ones
+    are allocated here."""
+    x = _c(x)
+    idx = _c(idx)
+    dev = _dev(x, idx)
+    T, H = x.shape
+    k = idx.shape[1]
+    _index(idx, (T, k), "idx")
+    N = T * k
+    out = dict(out or {})
+    shapes = dict(xd=((N, H), x.dtype), offsets=((num_experts + 1,), _U32),
+                  row_expert=((N,), _U32), row_token=((N,), _U32),
+                  token_row=((T, k), _U32))
+    for key, (shape, dtype) in shapes.items():
+        out[key] = _out(out.get(key), shape, dtype, dev, key)
+    check(lib().moe_dispatch_noalloc(
+        _p(x), _dt(x, "x"), T, H, num_experts, k, _p(idx), _p(out["xd"]),
+        _p(out["offsets"]), _p(out["row_expert"]), _p(out["row_token"]),
+        _p(out["token_row"]), _stream(dev)))
+    return out
+
+
 def moe_experts_forward(xd, offsets, w_gate, w_up, w_down, act=None, y=None):
     """SwiGLU experts over segments.  Returns y [N,H] (act [N,I] is the
     intermediate buffer; pass one in to keep it)."""

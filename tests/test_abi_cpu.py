@@ -368,14 +368,16 @@ def test_forward_clipped_rejects():
 
 
 CITES = ("guide, section", "guide, sections", "experts page",
-         "MindSpeed-Ops page", "No passage of the pages")
+         "MindSpeed-Ops page", "No passage of the pages",
+         "callers that cannot allocate")
 
 
 def test_every_declaration_cites_a_passage_or_says_it_has_none():
     """Each exported declaration's own comment names the passage of the
     pages that defines it (the ruDNN user guide's sections, the experts
     page, the MindSpeed-Ops page), or states that none does (host
-    arithmetic and instrumentation)."""
+    arithmetic and instrumentation), or, for the allocation-free variant
+    of an entry point, names the callers it is for."""
     src = open(HEADER).read()
     decls = re.finditer(
         r"/\*((?:(?!\*/).)*)\*/\s*(?:#define[^\n]*\n\s*)?"
