@@ -631,6 +631,8 @@ def summarize_trace(trace_dir):
             for r in csv.DictReader(f):
                 name = r["Name"].replace("(anonymous namespace)::", "")
                 name = name.replace("void ", "").split("(")[0]
+                if not name.startswith("moe::"):
+                    continue  # the input generator's kernels
                 print("| %s | %s | %.1f | %.1f | %.1f | %.1f | %.1f |" % (
                     name, r["Calls"], float(r["TotalDurationNs"]) / 1e3,
                     float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,

@@ -235,6 +235,25 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   }
 }
 
+// The mapping alone (no row copies), for callers whose expert GEMM reads
+// the token rows in place: entry i = (t, j) gets its row r from the scanned
+// table and its in-chunk rank (held in token_row by the count kernel).
+__global__ __launch_bounds__(256) void dispatch_map_kernel(
+    int64_t N, int k, int E, int64_t chunk, const uint32_t* __restrict__ idx,
+    const uint32_t* __restrict__ table, uint32_t* __restrict__ token_row,
+    uint32_t* __restrict__ row_expert, uint32_t* __restrict__ row_token) {
+  const int nb = E + 1;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t e = idx[i];
+    const uint32_t bin = e < (uint32_t)E ? e : (uint32_t)E;
+    const uint32_t r = table[(i / chunk) * nb + bin] + token_row[i];
+    token_row[i] = r;
+    row_expert[r] = e < (uint32_t)E ? e : 0xffffffffu;
+    row_token[r] = (uint32_t)(i / k);
+  }
+}
+
 template <typename V>
 hipError_t launch_scatter(const void* x, void* xd, int64_t T, int64_t bytes,
                           int k, int E, int64_t chunk, const uint32_t* idx,
@@ -318,6 +337,13 @@ hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,
   if (err != hipSuccess || T == 0) return err;  // T == 0: all offsets 0
   timing_mark(3, st);
 
+  if (!xd) {  // the mapping only
+    const int64_t blocks = (p.N + 255) / 256;
+    const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+    hipLaunchKernelGGL(dispatch_map_kernel, grid, dim3(256), 0, st, p.N, k, E,
+                       p.chunk, idx, table, token_row, row_expert, row_token);
+    return hipGetLastError();
+  }
   const int64_t es = dt == DT_F32 ? 4 : 2;
   const int64_t bytes = H * es;
   const uintptr_t al = (uintptr_t)x | (uintptr_t)xd;

@@ -20,7 +20,9 @@
 // prefix sum over the segments done by one wavefront) and exits if it has
 // none.  Logical tile order is expert-major, then column block, then row
 // block, so consecutive tiles share a weight tile; consecutive logical ids
-// are kept on one XCD so they share that XCD's L2.
+// run on one XCD so they share that XCD's L2 (runs of 16 dealt round robin
+// in the prefill and generic kernels, one contiguous range per XCD in the
+// decode kernel, whose tiles are all alike).
 //
 // MFMA path (bf16/f16, K a multiple of 8, 16-byte aligned operands):
 // 256 threads = 4 wavefronts in a WGM x (4/WGM) grid; v_mfma_f32_16x16x32
@@ -44,8 +46,8 @@
 namespace moe {
 namespace {
 
-// The plain tile map of locate_tile (BM-row blocks, the same logical order
-// and XCD ranges), run by each wavefront on its own and broadcast to its
+// The plain tile map (BM-row blocks, locate_tile's logical order, one
+// contiguous range of logical tiles per XCD), run by each wavefront on its own and broadcast to its
 // lanes: the kernel then keeps no tile record in LDS and needs no barrier
 // before its K loop, so four of its workgroups fit the 160 KB of LDS of a
 // CU (the record pushed each one just past a quarter).
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const typename Storage<D>::T* __restrict__ B1,
     typename Storage<D>::T* __restrict__ C,
     const uint32_t* __restrict__ offsets, int64_t N, int K, int NB, int E,
-    uint32_t ncol, int nseg, Swiglu sw = Swiglu{}) {
+    uint32_t ncol, int nseg, Swiglu sw = Swiglu{}, Gather ga = Gather{}) {
   using S = typename Storage<D>::T;
   using V = typename Frag<D>::V;
   constexpr int BK = 64;
@@ -147,6 +149,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const int q = tid + 256 * it, r = q >> 3, ch = q & 7;
     int64_t gr = row0 + r;
     gr = gr < hi ? gr : hi - 1;
+    if (GATEUP && ga.rows) {  // the token row of x, clamped into x
+      const int64_t tok = ga.rows[gr];
+      gr = tok < ga.xrows ? tok : ga.xrows - 1;
+    }
     pa[it] = A + gr * K + ch * 8;
     ka[it] = ch * 8;
   }
@@ -376,7 +382,8 @@ template <int D, int BM, int BN, int WGM, bool NTW>
 hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                             int E, const void* wg, const void* wu,
                             const void* wd, const uint32_t* offsets,
-                            void* act, void* y, hipStream_t st, Swiglu sw) {
+                            void* act, void* y, hipStream_t st, Swiglu sw,
+                            Gather ga = Gather{}) {
   using S = typename Storage<D>::T;
   {
     const uint32_t ncol = cdiv(I, BN / 2);
@@ -384,7 +391,7 @@ hipError_t launch_mfma_pair(const void* xd, int64_t N, int64_t H, int64_t I,
     hipLaunchKernelGGL((gemm_mfma_kernel<D, BM, BN, WGM, true, NTW>), dim3(grid),
                        dim3(256), 0, st, (const S*)xd, (const S*)wg,
                        (const S*)wu, (S*)act, offsets, N, (int)H, (int)I, E,
-                       ncol, E, sw);
+                       ncol, E, sw, ga);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -407,7 +414,7 @@ hipError_t launch_generic_pair(const void* xd, int64_t N, int64_t H,
   using S = typename Storage<D>::T;
   {
     const uint32_t ncol = cdiv(I, 32);
-    const uint32_t grid = tile_grid(ncol * (cdiv(N, 64) + (uint32_t)E));
+    const uint32_t grid = tile_grid_chunked(ncol * (cdiv(N, 64) + (uint32_t)E));
     hipLaunchKernelGGL((gemm_generic_kernel<D, true>), dim3(grid), dim3(256),
                        0, st, (const S*)xd, (const S*)wg, (const S*)wu,
                        (S*)act, offsets, N, (int)H, (int)I, E, ncol, E, sw);
@@ -416,32 +423,43 @@ hipError_t launch_generic_pair(const void* xd, int64_t N, int64_t H,
   }
   timing_mark(5, st);
   const uint32_t ncol = cdiv(H, 64);
-  const uint32_t grid = tile_grid(ncol * (cdiv(N, 64) + (uint32_t)E + 1));
+  const uint32_t grid = tile_grid_chunked(ncol * (cdiv(N, 64) + (uint32_t)E + 1));
   hipLaunchKernelGGL((gemm_generic_kernel<D, false>), dim3(grid), dim3(256),
                      0, st, (const S*)act, (const S*)wd, (const S*)wd,
                      (S*)y, offsets, N, (int)I, (int)H, E, ncol, E + 1);
   return hipGetLastError();
 }
 
+// Which MFMA kernels launch_mfma_dt takes: decode-sized 32-row tiles,
+// the prefill kernel of gemm_big.hip (row blocks of up to 320 rows x 256
+// columns, every buffer range under 2^31 bytes: the K-tail loads use offset
+// 2^31 as "past the end", so a row block's A range, 320 rows of K
+// elements, must stay below it), or 128 x 128 tiles.
+enum class MfmaPath { kDecode, kBig, kMid };
+MfmaPath mfma_path(int64_t N, int64_t H, int64_t I, int E) {
+  if (N < 96 * (int64_t)E) return MfmaPath::kDecode;
+  const int64_t lim = (int64_t)1 << 31;
+  if (H * I * 2 < lim && 320 * H * 2 < lim && 320 * I * 2 < lim)
+    return MfmaPath::kBig;
+  return MfmaPath::kMid;
+}
+
 template <int D>
 hipError_t launch_mfma_dt(const void* xd, int64_t N, int64_t H, int64_t I,
                           int E, const void* wg, const void* wu,
                           const void* wd, const uint32_t* offsets, void* act,
-                          void* y, hipStream_t st, Swiglu sw) {
-  // Few rows per expert (decode): short row blocks waste less work.
-  if (N < 96 * (int64_t)E)
-    return launch_mfma_pair<D, 32, 128, 1, MOE_DECODE_NT>(xd, N, H, I, E, wg, wu, wd,
-                                           offsets, act, y, st, sw);
-  // Prefill: row blocks of up to 320 rows x 256 columns when every buffer
-  // range fits 31 bits (the K-tail loads use offset 2^31 as "past the end",
-  // so a row block's A range, 320 rows of K elements, must stay below it).
-  const int64_t lim = (int64_t)1 << 31;
-  if (H * I * 2 < lim && 320 * H * 2 < lim && 320 * I * 2 < lim) {
-    return launch_experts_big(xd, D, N, H, I, E, wg, wu, wd, offsets, act, y,
-                              st, sw);
+                          void* y, hipStream_t st, Swiglu sw, Gather ga) {
+  switch (mfma_path(N, H, I, E)) {
+    case MfmaPath::kDecode:  // few rows per expert: short row blocks
+      return launch_mfma_pair<D, 32, 128, 1, MOE_DECODE_NT>(
+          xd, N, H, I, E, wg, wu, wd, offsets, act, y, st, sw, ga);
+    case MfmaPath::kBig:
+      return launch_experts_big(xd, D, N, H, I, E, wg, wu, wd, offsets, act,
+                                y, st, sw, ga);
+    default:
+      return launch_mfma_pair<D, 128, 128, 2, false>(
+          xd, N, H, I, E, wg, wu, wd, offsets, act, y, st, sw, ga);
   }
-  return launch_mfma_pair<D, 128, 128, 2, false>(xd, N, H, I, E, wg, wu, wd,
-                                          offsets, act, y, st, sw);
 }
 
 // Plain grouped NT product on MFMA (bf16/f16, K and NB multiples of 8,
@@ -481,7 +499,7 @@ hipError_t launch_nt_generic(const void* A, int64_t N, int64_t K,
   using S = typename Storage<D>::T;
   const int nseg = E + 1;
   const uint32_t ncol = cdiv(NB, 64);
-  const uint32_t grid = tile_grid(ncol * (cdiv(N, 64) + (uint32_t)nseg));
+  const uint32_t grid = tile_grid_chunked(ncol * (cdiv(N, 64) + (uint32_t)nseg));
   hipLaunchKernelGGL((gemm_generic_kernel<D, false>), dim3(grid), dim3(256),
                      0, st, (const S*)A, (const S*)B, (const S*)B, (S*)C,
                      offsets, N, (int)K, (int)NB, E, ncol, nseg);
@@ -507,21 +525,35 @@ hipError_t launch_grouped_nt(const void* A, int dt, int64_t N, int64_t K,
   }
 }
 
+bool experts_can_gather(int dt, int64_t N, int64_t H, int64_t I, int E,
+                        int64_t xrows, const void* x, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* act,
+                        const void* y) {
+  const uintptr_t al = (uintptr_t)x | (uintptr_t)w_gate | (uintptr_t)w_up |
+                       (uintptr_t)w_down | (uintptr_t)act | (uintptr_t)y;
+  const bool mfma = dt != DT_F32 && H % 8 == 0 && I % 8 == 0 && al % 16 == 0;
+  (void)N;
+  (void)E;
+  // x is addressed by 32-bit byte offsets in the prefill kernel
+  return mfma && xrows > 0 && xrows * H * 2 < ((int64_t)1 << 31);
+}
+
 hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
                           int64_t I, int E, const void* w_gate,
                           const void* w_up, const void* w_down,
                           const uint32_t* offsets, void* act, void* y,
-                          hipStream_t st, Swiglu sw) {
+                          hipStream_t st, Swiglu sw, Gather ga) {
   const uintptr_t al = (uintptr_t)xd | (uintptr_t)w_gate | (uintptr_t)w_up |
                        (uintptr_t)w_down | (uintptr_t)act | (uintptr_t)y;
   const bool mfma = dt != DT_F32 && H % 8 == 0 && I % 8 == 0 && al % 16 == 0;
   if (mfma) {
     if (dt == DT_BF16)
       return launch_mfma_dt<DT_BF16>(xd, N, H, I, E, w_gate, w_up, w_down,
-                                     offsets, act, y, st, sw);
+                                     offsets, act, y, st, sw, ga);
     return launch_mfma_dt<DT_F16>(xd, N, H, I, E, w_gate, w_up, w_down,
-                                  offsets, act, y, st, sw);
+                                  offsets, act, y, st, sw, ga);
   }
+  if (ga.rows) return hipErrorInvalidValue;  // callers check experts_can_gather
   switch (dt) {
     case DT_F32:
       return launch_generic_pair<DT_F32>(xd, N, H, I, E, w_gate, w_up, w_down,

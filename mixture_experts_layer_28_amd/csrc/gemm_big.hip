@@ -74,7 +74,9 @@ inline hipError_t allow_lds(const void* fn, std::atomic<uint64_t>& done) {
 // (row blocks of equal size), dealt to the XCDs in contiguous ranges; an expert
 // without rows writes zeros.  N is the row count of the dispatch, M passes
 // in `K`.
-template <int D, bool GATEUP, bool WG = false>
+// GATHER (gate+up only): A row r of the segments is row ga.rows[r] of the
+// token rows x = A [ga.xrows, K] instead of row r of the dispatched copy.
+template <int D, bool GATEUP, bool WG = false, bool GATHER = false>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const typename Storage<D>::T* __restrict__ A,
     const typename Storage<D>::T* __restrict__ B0,
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     typename Storage<D>::T* __restrict__ C,
     const uint32_t* __restrict__ offsets, int64_t N, int K, int NB, int E,
     uint32_t ncol, int nseg, float* __restrict__ Cw = nullptr,
-    Swiglu sw = Swiglu{}) {
+    Swiglu sw = Swiglu{}, Gather ga = Gather{}) {
   using S = typename Storage<D>::T;
   using V = typename Frag<D>::V;
   constexpr int WN = 2, NT = 512;
@@ -97,6 +99,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   S* sm = (S*)smem_raw;
   __shared__ TileInfo ti;
+  // GATHER: byte offset in x of each A row of the block (rows past it: OOB)
+  __shared__ uint32_t arow_off[GATHER ? kBM : 1];
 
   const int tid = threadIdx.x;
   const int64_t Mw = K;  // the weight-gradient form's M (rows of Cw[e])
@@ -158,12 +162,15 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     return;
   }
 
+  constexpr uint32_t OOB = 0x80000000u;
   const uint32_t rowbytes = (uint32_t)K * sizeof(S);
-  // the A resource spans this tile's rows only, so every range fits in
-  // 31 bits and OOB (2^31) is always past the end; in the weight-gradient
-  // form B's resource spans the tile's columns only, too
+  // the A resource spans this tile's rows only (or, gathering, the token
+  // rows x [xrows, K], under 2^31 bytes), so every range fits in 31 bits
+  // and OOB (2^31) is always past the end; in the weight-gradient form B's
+  // resource spans the tile's columns only, too
   const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(Ab + row0 * K, (uint64_t)arows * rowbytes);
+      GATHER ? make_rsrc(A, (uint64_t)ga.xrows * rowbytes)
+             : make_rsrc(Ab + row0 * K, (uint64_t)arows * rowbytes);
   const int64_t bcols = NB - n0 < kBN ? NB - n0 : kBN;
   const __amdgpu_buffer_rsrc_t rB0 =
       WG ? make_rsrc(Bb + n0 * K, (uint64_t)bcols * rowbytes)
@@ -172,7 +179,6 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       GATEUP ? make_rsrc(B1 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes)
              : rB0;
   const int64_t boff = WG ? 0 : n0;  // B row of the tile's first column
-  constexpr uint32_t OOB = 0x80000000u;
 
   const int wid = uniform(tid >> 6), lane = tid & 63;
   const int wm = wid / WN, wn = wid % WN;
@@ -185,7 +191,20 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 
   // ---- global -> LDS (direct) -------------------------------------------------
   // LDS stage: A rows 0..kBM-1 then B rows 0..255, 128 bytes per row; block
-  // b holds rows 8b..8b+7 of that sequence.
+  // b holds rows 8b..8b+7 of that sequence.  Gathering, A row r sits at
+  // the byte offset arow_off[r] of x (its token's row; rows past the block
+  // read zeros).
+  if constexpr (GATHER) {
+    for (int q = tid; q < kBM; q += NT) {
+      uint32_t off = OOB;
+      if (q < arows) {
+        const uint32_t tok = ga.rows[row0 + q];
+        if ((int64_t)tok < ga.xrows) off = tok * rowbytes;
+      }
+      arow_off[q] = off;
+    }
+    __syncthreads();
+  }
   auto dma = [&](int k0, int st) {
     S* base = sm + st * kStage;
 #pragma unroll
@@ -197,9 +216,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       const bool kin = kk < K;
       if (b < ABLK) {
         // blocks wholly past the row block stay unloaded (a uniform test)
+        const uint32_t ro = GATHER ? arow_off[r] : (uint32_t)r * rowbytes;
         if (8 * b < arows)
           buffer_load_lds16(rA, base + b * 512,
-                            kin ? (uint32_t)r * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
+                            kin ? ro + kk * (uint32_t)sizeof(S) : OOB);
       } else {
         const bool up = GATEUP && (b - ABLK) * 8 >= kBN / 2;  // uniform
         const int br = up ? r - kBN / 2 : r;
@@ -413,17 +433,29 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 template <int D, bool GATEUP>
 hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
                       const uint32_t* offsets, int64_t N, int K, int NB,
-                      int E, int nseg, hipStream_t st, Swiglu sw = Swiglu{}) {
+                      int E, int nseg, hipStream_t st, Swiglu sw = Swiglu{},
+                      Gather ga = Gather{}) {
   using S = typename Storage<D>::T;
+  const uint32_t ncol = cdiv(NB, GATEUP ? kBN / 2 : kBN);
+  // sum over segments of ceil(rows / kBM) <= ceil(N / kBM) + nseg
+  const uint32_t grid = tile_grid_chunked(ncol * (cdiv(N, kBM) + (uint32_t)nseg));
+  if (GATEUP && ga.rows) {
+    static std::atomic<uint64_t> attr{0};
+    hipError_t err = allow_lds(
+        (const void*)gemm_big_kernel<D, GATEUP, false, GATEUP>, attr);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP, false, GATEUP>),
+                       dim3(grid), dim3(512), kLds, st, (const S*)A,
+                       (const S*)B0, (const S*)B1, (S*)C, offsets, N, K, NB,
+                       E, ncol, nseg, nullptr, sw, ga);
+    return hipGetLastError();
+  }
   static std::atomic<uint64_t> attr{0};
   hipError_t err = allow_lds((const void*)gemm_big_kernel<D, GATEUP>, attr);
   if (err != hipSuccess) return err;
-  const uint32_t ncol = cdiv(NB, GATEUP ? kBN / 2 : kBN);
-  // sum over segments of ceil(rows / kBM) <= ceil(N / kBM) + nseg
-  const uint32_t grid = tile_grid(ncol * (cdiv(N, kBM) + (uint32_t)nseg));
   hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP>), dim3(grid), dim3(512),
                      kLds, st, (const S*)A, (const S*)B0, (const S*)B1, (S*)C,
-                     offsets, N, K, NB, E, ncol, nseg, nullptr, sw);
+                     offsets, N, K, NB, E, ncol, nseg, nullptr, sw, Gather{});
   return hipGetLastError();
 }
 
@@ -431,9 +463,9 @@ template <int D>
 hipError_t launch_pair(const void* xd, int64_t N, int64_t H, int64_t I,
                        int E, const void* wg, const void* wu, const void* wd,
                        const uint32_t* offsets, void* act, void* y,
-                       hipStream_t st, Swiglu sw) {
+                       hipStream_t st, Swiglu sw, Gather ga) {
   hipError_t err = launch_one<D, true>(xd, wg, wu, act, offsets, N, (int)H,
-                                       (int)I, E, E, st, sw);
+                                       (int)I, E, E, st, sw, ga);
   if (err != hipSuccess) return err;
   timing_mark(5, st);
   return launch_one<D, false>(act, wd, wd, y, offsets, N, (int)I, (int)H, E,
@@ -488,12 +520,12 @@ hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
                               int64_t I, int E, const void* w_gate,
                               const void* w_up, const void* w_down,
                               const uint32_t* offsets, void* act, void* y,
-                              hipStream_t st, Swiglu sw) {
+                              hipStream_t st, Swiglu sw, Gather ga) {
   if (dt == DT_BF16)
     return launch_pair<DT_BF16>(xd, N, H, I, E, w_gate, w_up, w_down, offsets,
-                                act, y, st, sw);
+                                act, y, st, sw, ga);
   return launch_pair<DT_F16>(xd, N, H, I, E, w_gate, w_up, w_down, offsets,
-                             act, y, st, sw);
+                             act, y, st, sw, ga);
 }
 
 }  // namespace moe

@@ -6,6 +6,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+
 namespace moe {
 
 struct TileInfo {
@@ -31,6 +32,9 @@ __device__ __forceinline__ void segment(const uint32_t* __restrict__ offsets,
   }
 }
 
+// Consecutive logical tiles per XCD chunk (locate_tile).
+constexpr uint32_t kXcdChunk = 16;
+
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -48,13 +52,17 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 // one shorter) or, with `balanced`, made of the ceil(R / 32) units of 32
 // rows (the last unit partial) dealt out as evenly as possible, so that no
 // row block is a thin remainder (BM a multiple of 32).  Pass 1 totals the
-// real tiles; they are then split evenly over the 8 XCDs (hardware deals
-// workgroup b to XCD b % 8; each XCD takes a contiguous range of logical
-// ids, so tiles that share operands share an L2), and pass 2 finds the
-// segment of logical tile L.  Inside a segment, tiles go in groups of up to
-// 8 row blocks: all column blocks of a group before the next group, the row
+// real tiles; they are then dealt to the 8 XCDs (hardware deals workgroup b
+// to XCD b % 8) in chunks of kXcdChunk consecutive logical tiles, round
+// robin: the tiles of one chunk run side by side on one XCD and share its
+// L2, and every XCD gets a mix of large and small tiles.  (Contiguous
+// ranges of equal tile counts per XCD left the XCD holding the most large
+// tiles of a skewed routing ~9 % above the mean; the fine-grained expert
+// stage ran 7 % faster with chunks of 16.)  Pass 2 finds the segment of
+// logical tile L.  Inside a segment, tiles go in groups of up to 8 row
+// blocks: all column blocks of a group before the next group, the row
 // blocks of one column block consecutive.
-// G must be a multiple of 8 and at least 8 * ceil(tiles / 8).
+// G must be at least tile_grid(tiles).
 __device__ inline void locate_tile(uint32_t b, uint32_t G,
                                    const uint32_t* __restrict__ offsets,
                                    int E, int64_t N, int BM, uint32_t ncol,
@@ -69,9 +77,9 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
     const uint32_t cnt = (uint32_t)((hi - lo + BM - 1) / BM) * ncol;
     total += __shfl(wave_inclusive_sum(cnt, lane), 63, 64);
   }
-  const uint32_t per = (total + 7u) / 8u, local = b / 8u;
-  const uint32_t L = (b % 8u) * per + local;
-  if (local >= per || L >= total) return;
+  const uint32_t local = b / 8u, q = local / kXcdChunk;
+  const uint32_t L = (q * 8u + b % 8u) * kXcdChunk + local % kXcdChunk;
+  if (L >= total) return;
   (void)G;
   uint32_t base = 0;
   for (int s0 = 0; s0 < nseg; s0 += 64) {
@@ -118,8 +126,15 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
 }
 
 // Grid for an upper bound of `tiles` tiles: a multiple of 8 with at least
-// ceil(tiles / 8) workgroups on every XCD.
+// ceil(tiles / 8) workgroups on every XCD (the per-wave tile map of the
+// decode kernels, which keeps contiguous XCD ranges).
 inline uint32_t tile_grid(uint32_t tiles) { return 8u * ((tiles + 7u) / 8u); }
+// ... for locate_tile's chunked deal: every XCD holds up to ceil(chunks / 8)
+// chunks of kXcdChunk tiles.
+inline uint32_t tile_grid_chunked(uint32_t tiles) {
+  const uint32_t nch = (tiles + kXcdChunk - 1) / kXcdChunk;
+  return 8u * kXcdChunk * ((nch + 7u) / 8u);
+}
 
 __device__ __forceinline__ int swz(int r) { return r & 7; }
 

@@ -61,6 +61,8 @@ struct DispatchPlan {
 };
 DispatchPlan plan_dispatch(int64_t T, int64_t E, int64_t k);
 
+// xd == nullptr: the mapping only, no row copies (the expert GEMM then
+// reads the token rows in place through row_token).
 hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,
                            int E, int k, const uint32_t* idx, void* xd,
                            uint32_t* offsets, uint32_t* row_expert,
@@ -82,11 +84,28 @@ struct Swiglu {
   float limit = -1.0f;
 };
 
+// Rows of the gate+up product's A operand read in place from the token
+// rows: dispatched row r of the segments is row rows[r] of x [xrows, H]
+// (the dispatch's row_token), so the dispatched copy xd is never
+// materialised.  rows == nullptr: A is xd itself.
+struct Gather {
+  const uint32_t* rows = nullptr;
+  int64_t xrows = 0;
+};
+
 hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
                           int64_t I, int E, const void* w_gate,
                           const void* w_up, const void* w_down,
                           const uint32_t* offsets, void* act, void* y,
-                          hipStream_t st, Swiglu sw = Swiglu{});
+                          hipStream_t st, Swiglu sw = Swiglu{},
+                          Gather ga = Gather{});
+// Whether launch_experts can take its A rows through a Gather for these
+// sizes and pointers (the MFMA paths, with x [xrows, H] addressable by
+// 32-bit byte offsets); otherwise xd must be materialised.
+bool experts_can_gather(int dt, int64_t N, int64_t H, int64_t I, int E,
+                        int64_t xrows, const void* x, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* act,
+                        const void* y);
 
 // 256x256-tile kernels for prefill-sized segments (bf16/f16, H and I
 // multiples of 8, 16-byte aligned, every per-expert weight matrix and 256
@@ -95,7 +114,8 @@ hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,
                               int64_t I, int E, const void* w_gate,
                               const void* w_up, const void* w_down,
                               const uint32_t* offsets, void* act, void* y,
-                              hipStream_t st, Swiglu sw = Swiglu{});
+                              hipStream_t st, Swiglu sw = Swiglu{},
+                              Gather ga = Gather{});
 
 // One plain grouped NT product C[r, :] = A[r, :] . B[e]^T for the rows r of
 // segment e (A [N,K], B [E,NB,K], C [N,NB], all of dtype dt); rows past

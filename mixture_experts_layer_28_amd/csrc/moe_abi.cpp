@@ -273,15 +273,26 @@ int run_forward(const char* f, const void* x, int dt, int ldt, int64_t T,
   hipError_t err = route(idx, w, st);
   std::snprintf(what, sizeof(what), "%s(route)", f);
   if (err != hipSuccess) return hip_status(err, what);
+  // Where the MFMA kernels can read the token rows in place, dispatch
+  // writes only the mapping and the gate+up GEMM gathers its A rows from x
+  // through row_token (the same values as the copies, so the same result).
+  const bool gather = moe::experts_can_gather(dt, N, H, I, (int)E, T, x,
+                                              w_gate, w_up, w_down, act, y);
   moe::timing_mark(1, st);
-  err = moe::launch_dispatch(x, dt, T, H, (int)E, (int)top_k, idx, xd,
-                             offsets, row_expert, row_token, token_row, dws,
+  err = moe::launch_dispatch(x, dt, T, H, (int)E, (int)top_k, idx,
+                             gather ? nullptr : xd, offsets, row_expert,
+                             row_token, token_row, dws,
                              moe::plan_dispatch(T, E, top_k), st);
   std::snprintf(what, sizeof(what), "%s(dispatch)", f);
   if (err != hipSuccess) return hip_status(err, what);
   moe::timing_mark(4, st);
-  err = moe::launch_experts(xd, dt, N, H, I, (int)E, w_gate, w_up, w_down,
-                            offsets, act, y, st, sw);
+  moe::Gather ga;
+  if (gather) {
+    ga.rows = row_token;
+    ga.xrows = T;
+  }
+  err = moe::launch_experts(gather ? x : xd, dt, N, H, I, (int)E, w_gate,
+                            w_up, w_down, offsets, act, y, st, sw, ga);
   std::snprintf(what, sizeof(what), "%s(experts)", f);
   if (err != hipSuccess) return hip_status(err, what);
   moe::timing_mark(6, st);
