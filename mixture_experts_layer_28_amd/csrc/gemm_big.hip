@@ -96,6 +96,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   constexpr int BLK = NBLK / 8;                   // ... per wave
   static_assert(NBLK % 8 == 0, "blocks per wave");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up halves");
+  static_assert(FN == 8, "an 8-column group per lane: one 16-byte vector");
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   S* sm = (S*)smem_raw;
   __shared__ TileInfo ti;
@@ -182,6 +183,11 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 
   const int wid = uniform(tid >> 6), lane = tid & 63;
   const int wm = wid / WN, wn = wid % WN;
+  // B chunk rotation: the plain products read B rows 8 apart in one
+  // fragment (brow0 below), so their 16-byte chunks rotate by row / 8 and
+  // the 8 lanes of each LDS pass hit 8 different chunk slots; the gate+up
+  // product reads consecutive rows and rotates by row, like A.
+  auto swzb = [](int r) { return GATEUP ? swz(r) : (r >> 3) & 7; };
 
   // MFMA row tiles of this wave: t16 tiles over 4 wave rows, the first
   // t16 % 4 rows taking one more; waves wm and wm + 2 share a SIMD.
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     for (int j = 0; j < BLK; ++j) {
       const int b = wid + 8 * j;
       const int r = 8 * (b < ABLK ? b : b - ABLK) + (lane >> 3);  // row within A or B
-      const int c = (lane & 7) ^ swz(r);
+      const int c = (lane & 7) ^ (b < ABLK ? swz(r) : swzb(r));
       const int kk = k0 + c * 8;
       const bool kin = kk < K;
       if (b < ABLK) {
@@ -230,15 +236,22 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   };
 
   // ---- fragments, MFMAs and the epilogue ---------------------------------------
-  auto brow = [&](int j) -> int {
-    if (GATEUP) {
-      constexpr int H2 = FN / 2;
-      return (j < H2 ? wn * (TN / 2) + j * 16
-                     : kBN / 2 + wn * (TN / 2) + (j - H2) * 16) +
-             (lane & 15);
-    }
-    return wn * TN + j * 16 + (lane & 15);
+  // The B tile row (LDS row) feeding column j of a lane's MFMA tiles is
+  // brow0 + bstep(j), and all of them share one chunk rotation, so every
+  // B fragment read is one base address plus a constant.
+  // Plain products: column j of a lane is output column (lane % 16) * 8 + j
+  // of the wave's 128, so after the K loop each lane holds 8 consecutive
+  // outputs of a row and the epilogue stores them as one 16-byte vector.
+  // Gate+up: column j < 4 is gate column 16 j + lane % 16 of the wave's 64
+  // act columns and j >= 4 the up column of the same act column (this
+  // product keeps consecutive rows per fragment: the permuted form cost it
+  // registers and spills).
+  const int brow0 = wn * (GATEUP ? TN / 2 : TN) + (lane & 15) * (GATEUP ? 1 : FN);
+  auto bstep = [](int j) -> int {
+    constexpr int H2 = FN / 2;
+    return GATEUP ? (j < H2 ? 16 * j : kBN / 2 + 16 * (j - H2)) : j;
   };
+  const int bswz = swzb(brow0);
 
   const int nk = (K + kBK - 1) / kBK;
   // The K loop and epilogue of a wave with FMC MFMA row tiles (0: it only
@@ -263,8 +276,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int r = brow(j);
-        fb[j] = *(const V*)&Bs[r * kBK + ((c ^ swz(r)) << 3)];
+        fb[j] = *(const V*)&Bs[(brow0 + bstep(j)) * kBK + ((c ^ bswz) << 3)];
       }
     };
     auto mma = [&](const V* fa, const V* fb) {
@@ -322,8 +334,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       auto read_b = [&](int st, int half, int j) -> V {
         const S* Bs = sm + st * kStage + kBM * kBK;
         const int c = half * 4 + (lane >> 4);
-        const int r = brow(j);
-        return *(const V*)&Bs[r * kBK + ((c ^ swz(r)) << 3)];
+        return *(const V*)&Bs[(brow0 + bstep(j)) * kBK + ((c ^ bswz) << 3)];
       };
       V fa[FMC], fb[FN];
       auto mma_cols = [&](int st2, int half2, bool reload) {
@@ -387,13 +398,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       for (int q = 0; q < 4; ++q) {
         const int64_t r = row0 + tr0 + i * 16 + (lane >> 4) * 4 + q;
         if (r >= tend) continue;
+        // NB is a multiple of 8: a lane's group of 8 consecutive columns is
+        // wholly inside or wholly past NB
         if constexpr (WG) {
           // M arrives as the kernel's K argument; K is now the expert's rows
           float* cw = Cw + ((int64_t)e * Mw + r) * NB;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int64_t c = n0 + wn * TN + j * 16 + (lane & 15);
-            if (c < NB) cw[c] = acc[i][j][q];
+          const int64_t c0 = n0 + wn * TN + (lane & 15) * FN;
+          if (c0 < NB) {
+            *(f32x4*)(cw + c0) = f32x4{acc[i][0][q], acc[i][1][q],
+                                       acc[i][2][q], acc[i][3][q]};
+            *(f32x4*)(cw + c0 + 4) = f32x4{acc[i][4][q], acc[i][5][q],
+                                           acc[i][6][q], acc[i][7][q]};
           }
           continue;
         }
@@ -410,10 +425,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
             }
           }
         } else {
+          const int64_t c0 = n0 + wn * TN + (lane & 15) * FN;
+          if (c0 < NB) {
+            V v;
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int64_t c = n0 + wn * TN + j * 16 + (lane & 15);
-            if (c < NB) crow[c] = from_f32<D>(acc[i][j][q]);
+            for (int j = 0; j < FN; ++j) v[j] = from_f32<D>(acc[i][j][q]);
+            *(V*)(crow + c0) = v;
           }
         }
       }
