@@ -65,6 +65,150 @@ inline hipError_t allow_lds(const void* fn, std::atomic<uint64_t>& done) {
   return err;
 }
 
+// ---- tiles of at most kTinyRows rows ---------------------------------------
+// A row block this short has almost no MFMA work: its cost is streaming the
+// 256 weight rows of its column block over the whole K.  Such a tile keeps
+// three LDS stages of (kTinyRows + 256) rows x 64 K in flight instead of
+// the main loop's two stages of up to 576 rows, so its loads go out two
+// stages ahead of their use, and every wave computes all the tile's row
+// tiles for 32 of its 256 columns (gate+up: 16 act columns, gate and up).
+// (A non-inlined call cost the main loop SGPR spills; inlined, the
+// fine-grained forward runs ~1 % faster and the Mixtral-shaped one is
+// unchanged.)
+constexpr int kTinyRows = 64;
+constexpr int kTinyStage = (kTinyRows + kBN) * kBK;  // elements per stage
+constexpr int kTinyStages = 3;
+static_assert(kTinyStages * kTinyStage * 2 <= (int)kLds, "tiny stages fit");
+
+// A raw buffer resource from a pointer and size every lane agrees on.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void* p,
+                                                            uint64_t bytes) {
+  const uint64_t u = (uint64_t)uniform((int64_t)(uintptr_t)p);
+  return make_rsrc((const void*)(uintptr_t)u, (uint64_t)uniform((int64_t)bytes));
+}
+
+template <int D, bool GATEUP, bool GATHER>
+__device__ __forceinline__ void tiny_tile(
+    const typename Storage<D>::T* A, const typename Storage<D>::T* B0,
+    const typename Storage<D>::T* B1, typename Storage<D>::T* C,
+    const uint32_t* grows, int64_t xrows, int64_t row0, int arows,
+    int64_t n0, int e, int K, int NB, Swiglu sw) {
+  using S = typename Storage<D>::T;
+  using V = typename Frag<D>::V;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  S* sm = (S*)smem_raw;
+  constexpr uint32_t OOB = 0x80000000u;
+  row0 = uniform(row0);
+  arows = uniform(arows);
+  n0 = uniform(n0);
+  e = uniform(e);
+  K = uniform(K);
+  NB = uniform(NB);
+  const uint32_t rowbytes = (uint32_t)K * sizeof(S);
+  const __amdgpu_buffer_rsrc_t rA =
+      GATHER ? make_rsrc_u(A, (uint64_t)xrows * rowbytes)
+             : make_rsrc_u(A + row0 * K, (uint64_t)arows * rowbytes);
+  const __amdgpu_buffer_rsrc_t rB0 =
+      make_rsrc_u(B0 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes);
+  const __amdgpu_buffer_rsrc_t rB1 =
+      GATEUP ? make_rsrc_u(B1 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes)
+             : rB0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = uniform(tid >> 6);
+  // this lane's A row (its wave's one A block) and its byte offset
+  const int ar = 8 * wid + (lane >> 3);
+  uint32_t aoff = OOB;
+  if (ar < arows) {
+    if (GATHER) {
+      const uint32_t tok = grows[row0 + ar];
+      if ((int64_t)tok < xrows) aoff = tok * rowbytes;
+    } else {
+      aoff = (uint32_t)ar * rowbytes;
+    }
+  }
+  // every wave issues exactly 5 loads per stage (one A block, four B
+  // blocks; A rows past the tile read zeros), so vmcnt counts stages
+  auto dma = [&](int k0, int st) {
+    S* base = sm + st * kTinyStage;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int b = wid + 8 * j;
+      const int r = 8 * (j == 0 ? b : b - 8) + (lane >> 3);
+      const int kk = k0 + ((lane & 7) ^ swz(r)) * 8;
+      const bool kin = kk < K;
+      if (j == 0) {
+        buffer_load_lds16(rA, base + b * 512,
+                          kin && aoff != OOB ? aoff + kk * (uint32_t)sizeof(S) : OOB);
+      } else {
+        const bool up = GATEUP && r >= kBN / 2;  // uniform per block
+        const int br = up ? r - kBN / 2 : r;
+        buffer_load_lds16(up ? rB1 : rB0, base + b * 512,
+                          kin ? (uint32_t)(n0 + br) * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
+      }
+    }
+  };
+  const int t16 = (arows + 15) >> 4;  // 1 .. 4 row tiles, all in every wave
+  // B rows of this wave's two column tiles
+  const int b0 = GATEUP ? wid * 16 : wid * 32;
+  const int b1 = GATEUP ? kBN / 2 + wid * 16 : wid * 32 + 16;
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = (K + kBK - 1) / kBK;
+  dma(0, 0);
+  if (nk > 1) dma(kBK, 1);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt landed everywhere; everyone finished reading stage kt - 1
+    if (kt + 1 < nk)
+      asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 2 < nk) dma((kt + 2) * kBK, (kt + 2) % kTinyStages);
+    const S* As = sm + (kt % kTinyStages) * kTinyStage;
+    const S* Bs = As + kTinyRows * kBK;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c = half * 4 + (lane >> 4);
+      const int r0 = b0 + (lane & 15), r1 = b1 + (lane & 15);
+      const V fb0 = *(const V*)&Bs[r0 * kBK + ((c ^ swz(r0)) << 3)];
+      const V fb1 = *(const V*)&Bs[r1 * kBK + ((c ^ swz(r1)) << 3)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < t16) {
+          const int r = i * 16 + (lane & 15);
+          const V fa = *(const V*)&As[r * kBK + ((c ^ swz(r)) << 3)];
+          acc[i][0] = Frag<D>::mma(fa, fb0, acc[i][0]);
+          acc[i][1] = Frag<D>::mma(fa, fb1, acc[i][1]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= t16) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = i * 16 + (lane >> 4) * 4 + q;
+      if (rr >= arows) continue;
+      S* crow = C + (row0 + rr) * NB;
+      if (GATEUP) {
+        const int64_t c = n0 + wid * 16 + (lane & 15);
+        if (c < NB) {
+          const float g = to_f32<D>(from_f32<D>(acc[i][0][q]));
+          const float u = to_f32<D>(from_f32<D>(acc[i][1][q]));
+          crow[c] = from_f32<D>(swiglu_act(g, u, sw));
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int64_t c = n0 + wid * 32 + jj * 16 + (lane & 15);
+          if (c < NB) crow[c] = from_f32<D>(acc[i][jj][q]);
+        }
+      }
+    }
+  }
+}
+
 // WG: the weight-gradient form.  Per expert e with rows [lo, hi) of a
 // dispatch, Cw[e] [M, NB] (FP32) = A_e . B_e^T with A_e = A + (lo + 8e) * M
 // holding [M, Kp] and B_e = B0 + (lo + 8e) * NB holding [NB, Kp], Kp =
@@ -160,6 +304,11 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       const int64_t r = row0 + q / TCOLS, c = n0 + q % TCOLS;
       if (r < tend && c < NB) C[r * NB + c] = from_f32<D>(0.0f);
     }
+    return;
+  }
+  if (!WG && arows <= kTinyRows) {
+    tiny_tile<D, GATEUP, GATHER>(A, B0, B1, C, ga.rows, ga.xrows, row0,
+                                 arows, n0, e, K, NB, sw);
     return;
   }
 

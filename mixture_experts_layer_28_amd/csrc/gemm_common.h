@@ -32,15 +32,10 @@ __device__ __forceinline__ void segment(const uint32_t* __restrict__ offsets,
   }
 }
 
-// Consecutive logical tiles per XCD chunk (locate_tile).
-#ifndef MOE_XCD_CHUNK
-#define MOE_XCD_CHUNK 16
-#endif
-#ifndef MOE_SMALL_LAST
-#define MOE_SMALL_LAST 0
-#endif
-constexpr uint32_t kXcdChunk = MOE_XCD_CHUNK;
-constexpr int64_t kSmallLast = MOE_SMALL_LAST;
+// Consecutive logical tiles per XCD chunk (locate_tile).  Chunks of 8 and
+// 32, groups of 2, 4 or 16 row blocks and the segments of fewer than 64 or
+// 320 rows placed last measured the same or slower.
+constexpr uint32_t kXcdChunk = 16;
 
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 #pragma unroll
@@ -89,12 +84,10 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
   if (L >= total) return;
   (void)G;
   uint32_t base = 0;
-  for (int part = 0; part < (kSmallLast > 0 ? 2 : 1); ++part)
   for (int s0 = 0; s0 < nseg; s0 += 64) {
     const int s = s0 + lane;
     int64_t lo, hi;
     segment(offsets, s, E, N, nseg, &lo, &hi);
-    if (kSmallLast > 0 && ((hi - lo < kSmallLast) != (part == 1))) hi = lo;
     const uint32_t nt = (uint32_t)((hi - lo + BM - 1) / BM);
     const uint32_t cnt = nt * ncol;
     const uint32_t inc = wave_inclusive_sum(cnt, lane);
