@@ -330,13 +330,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
              : rB0;
   const int64_t boff = WG ? 0 : n0;  // B row of the tile's first column
 
-  const int wid = uniform(tid >> 6), lane = tid & 63;
+  const int wid = uniform(tid >> 6) & 7, lane = tid & 63;
   const int wm = wid / WN, wn = wid % WN;
-  // B chunk rotation: the plain products read B rows 8 apart in one
-  // fragment (brow0 below), so their 16-byte chunks rotate by row / 8 and
-  // the 8 lanes of each LDS pass hit 8 different chunk slots; the gate+up
-  // product reads consecutive rows and rotates by row, like A.
-  auto swzb = [](int r) { return GATEUP ? swz(r) : (r >> 3) & 7; };
+  // B rows in LDS.  The plain products read B rows 8 apart in one
+  // fragment (brow0 below), so B row r = 64a + 8b + c is kept at LDS row
+  // 64a + 8c + b: a fragment read then covers 8 consecutive LDS rows, whose
+  // chunks rotate by LDS row like A's (rotating rows 8 apart by row / 8
+  // instead left bank conflicts).  The gate+up product reads consecutive
+  // rows and keeps them in order.
+  auto bsrc = [](int R) {  // B tile row held at LDS row R (an involution)
+    return GATEUP ? R : (R & ~63) | ((R & 7) << 3) | ((R >> 3) & 7);
+  };
 
   // MFMA row tiles of this wave: t16 tiles over 4 wave rows, the first
   // t16 % 4 rows taking one more; waves wm and wm + 2 share a SIMD.
@@ -362,24 +366,27 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   }
   auto dma = [&](int k0, int st) {
     S* base = sm + st * kStage;
+    // branch-free: which slots hold A or B blocks, and which B rows are
+    // up rows, is fixed per unrolled slot (wid < 8), so the issue is
+    // straight-line code (it was a chain of uniform branches per block)
+    constexpr int AJ = ABLK / 8;  // A blocks per wave: wave w takes w + 8 j
 #pragma unroll
     for (int j = 0; j < BLK; ++j) {
-      const int b = wid + 8 * j;
-      const int r = 8 * (b < ABLK ? b : b - ABLK) + (lane >> 3);  // row within A or B
-      const int c = (lane & 7) ^ (b < ABLK ? swz(r) : swzb(r));
-      const int kk = k0 + c * 8;
-      const bool kin = kk < K;
-      if (b < ABLK) {
-        // blocks wholly past the row block stay unloaded (a uniform test)
+      if (j < AJ) {
+        const int b = wid + 8 * j;  // A block; rows past the tile read zeros
+        const int r = 8 * b + (lane >> 3);
+        const int kk = k0 + ((lane & 7) ^ swz(r)) * 8;
         const uint32_t ro = GATHER ? arow_off[r] : (uint32_t)r * rowbytes;
-        if (8 * b < arows)
-          buffer_load_lds16(rA, base + b * 512,
-                            kin ? ro + kk * (uint32_t)sizeof(S) : OOB);
+        buffer_load_lds16(rA, base + b * 512,
+                          kk < K ? ro + kk * (uint32_t)sizeof(S) : OOB);
       } else {
-        const bool up = GATEUP && (b - ABLK) * 8 >= kBN / 2;  // uniform
-        const int br = up ? r - kBN / 2 : r;
-        buffer_load_lds16(up ? rB1 : rB0, base + b * 512,
-                          kin ? (uint32_t)(boff + br) * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
+        const int bb = wid + 8 * (j - AJ);  // B block
+        const int R = 8 * bb + (lane >> 3);
+        const int kk = k0 + ((lane & 7) ^ swz(R)) * 8;
+        const bool up = GATEUP && (j - AJ) * 64 >= kBN / 2;  // rows >= 128
+        const int br = up ? R - kBN / 2 : bsrc(R);
+        buffer_load_lds16(up ? rB1 : rB0, base + (ABLK + bb) * 512,
+                          kk < K ? (uint32_t)(boff + br) * rowbytes + kk * (uint32_t)sizeof(S) : OOB);
       }
     }
   };
@@ -395,12 +402,15 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   // act columns and j >= 4 the up column of the same act column (this
   // product keeps consecutive rows per fragment: the permuted form cost it
   // registers and spills).
-  const int brow0 = wn * (GATEUP ? TN / 2 : TN) + (lane & 15) * (GATEUP ? 1 : FN);
+  // (Plain products: B row wn * 128 + (lane % 16) * 8 + j sits at LDS row
+  // wn * 128 + 64 * ((lane / 8) % 2) + 8 j + lane % 8.)
+  const int brow0 = GATEUP ? wn * (TN / 2) + (lane & 15)
+                           : wn * TN + ((lane >> 3) & 1) * 64 + (lane & 7);
   auto bstep = [](int j) -> int {
     constexpr int H2 = FN / 2;
-    return GATEUP ? (j < H2 ? 16 * j : kBN / 2 + 16 * (j - H2)) : j;
+    return GATEUP ? (j < H2 ? 16 * j : kBN / 2 + 16 * (j - H2)) : 8 * j;
   };
-  const int bswz = swzb(brow0);
+  const int bswz = swz(brow0);
 
   const int nk = (K + kBK - 1) / kBK;
   // The K loop and epilogue of a wave with FMC MFMA row tiles (0: it only
@@ -449,19 +459,45 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       // that skips the barrier joins the barrier path just before the
       // second-half MFMAs, and the wait counts merged at that join made
       // them wait for the next stage's fragment reads as well.
+      // Scheduling groups interleave the loads with the MFMAs: one MFMA
+      // between consecutive LDS fragment reads before the barrier, and
+      // after it one MFMA between consecutive operand loads, then between
+      // the fragment reads.  Without them the compiler issued every load
+      // and read first and the matrix pipe idled while both waves of a
+      // SIMD did so (Mixtral-shaped expert stage 5 % faster with them).
+      // The operand loads are issued unconditionally (the stage past the
+      // last one reads zeros into a buffer nothing reads), so the region
+      // after the barrier is one basic block the groups can order.
       V fa0[FMC], fb0[FN], fa1[FMC], fb1[FN];
       read_frags(0, 0, fa0, fb0);
       for (int kt = 0; kt + 1 < nk; ++kt) {
         const int st = kt & 1;
         read_frags(st, 1, fa1, fb1);
         mma(fa0, fb0);
+#pragma unroll
+        for (int q = 0; q < FMC + FN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FMC * FN - (FMC + FN), 0);
         wait_vmem();
         __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
-        if (kt + 2 < nk) dma((kt + 2) * kBK, st);
+        dma((kt + 2) * kBK, st);  // past the last stage: zeros, never read
         read_frags(st ^ 1, 0, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
         mma(fa1, fb1);
+#pragma unroll
+        for (int q = 0; q < BLK; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+        }
+#pragma unroll
+        for (int q = 0; q < FMC + FN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FMC * FN > BLK + FMC + FN ? FMC * FN - BLK - FMC - FN : 0, 1);
       }
+      wait_vmem();  // the zero loads past the last stage
       read_frags((nk - 1) & 1, 1, fa1, fb1);
       mma(fa0, fb0);
       mma(fa1, fb1);
@@ -517,10 +553,16 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         mma_cols(st, 1, true);  // first half; fragments of the second
         wait_vmem();
         __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
-        if (kt + 2 < nk) dma((kt + 2) * kBK, st);
-        __builtin_amdgcn_sched_barrier(0);
+        dma((kt + 2) * kBK, st);  // past the last stage: zeros, never read
         mma_cols(st ^ 1, 0, true);  // second half; fragments of the next
+        // one MFMA between consecutive operand loads, as above
+#pragma unroll
+        for (int q = 0; q < BLK; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
       }
+      wait_vmem();  // the zero loads past the last stage
       mma_cols((nk - 1) & 1, 1, true);
       mma_cols(0, 0, false);
     } else {
