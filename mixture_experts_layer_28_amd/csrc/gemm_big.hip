@@ -479,7 +479,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, FMC * FN - (FMC + FN), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FMC * FN > FMC + FN ? FMC * FN - (FMC + FN) : 0, 0);
         wait_vmem();
         __syncthreads();  // stage kt+1 landed everywhere; stage kt fully read
         dma((kt + 2) * kBK, st);  // past the last stage: zeros, never read
