@@ -686,6 +686,11 @@ def summarize_counters(run_dir):
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         if c in counters:
             derived.append(c + " MB")
+    # wave-state counters over SQ_WAVE_CYCLES (all in quad-cycles summed
+    # over the SIMDs): the share of the waves' resident time spent so
+    shares = [c for c in WAVE_SHARES if c in counters]
+    if "SQ_WAVE_CYCLES" in counters:
+        derived += ["%s %%" % WAVE_SHARES[c] for c in shares]
     cols = ["kernel", "dispatches", "mean us"] + counters + derived
     print("| " + " | ".join(cols) + " |")
     print("|" + "---|" * len(cols))
@@ -706,7 +711,17 @@ def summarize_counters(run_dir):
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             if c + " MB" in derived:
                 row.append("%.1f" % (mean.get(c, 0) * 1024 / 1e6))
+        if "SQ_WAVE_CYCLES" in counters:
+            wc = mean.get("SQ_WAVE_CYCLES", 0)
+            row += ["%.1f" % (100.0 * mean.get(c, 0) / wc) if wc else ""
+                    for c in shares]
         print("| " + " | ".join(row) + " |")
+
+
+# counter -> column label of its share of SQ_WAVE_CYCLES
+WAVE_SHARES = {"SQ_WAIT_ANY": "waiting", "SQ_WAIT_INST_ANY": "waiting on a dependency",
+               "SQ_ACTIVE_INST_ANY": "issuing", "SQ_ACTIVE_INST_VMEM": "issuing VMEM",
+               "SQ_ACTIVE_INST_LDS": "issuing LDS", "SQ_WAIT_INST_LDS": "waiting to issue LDS"}
 
 
 def recorded_traffic(key):
