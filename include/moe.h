@@ -506,11 +506,17 @@ int moe_dispatch_backward(const void* grad_xd, int dt, int64_t N, int64_t T,
  * on this thread records
  * events[0] on its stream before its first kernel and events[i] right
  * after its i-th kernel, so the elapsed time between events[i-1] and
- * events[i] is kernel i.  The kernels of both forwards, in order: 1 route
+ * events[i] is kernel i.  The kernels of the forwards, in order: 1 route
  * (softmax or group-limited sigmoid), 2 dispatch count, 3 dispatch scan,
- * 4 dispatch scatter, 5 gate+up GEMM with SwiGLU, 6 down GEMM, 7 combine.
- * count must be 0 or MOE_TIMING_EVENTS.  The library does not own the
- * events; the caller keeps them alive while recording is on.
+ * 4 dispatch (the mapping alone where the gate+up GEMM reads the token
+ * rows in place, else the row scatter), 5 gate+up GEMM with SwiGLU,
+ * 6 down GEMM, 7 combine.  Where the softmax forwards route and count in
+ * one launch, that launch is kernel 1 and events[1] and events[2] are
+ * recorded back to back (interval 2 holds no kernel).  A NULL entry
+ * skips that mark (each recorded event costs a few microseconds of GPU
+ * time; a caller timing one kernel sets only its two events).  count must
+ * be 0 or MOE_TIMING_EVENTS.  The library does not own the events; the
+ * caller keeps them alive while recording is on.
  */
 #define MOE_TIMING_EVENTS 8
 int moe_set_timing_events(void* const* events, int count);

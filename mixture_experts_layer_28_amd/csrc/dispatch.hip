@@ -319,9 +319,9 @@ hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,
                            uint32_t* offsets, uint32_t* row_expert,
                            uint32_t* row_token, uint32_t* token_row,
                            void* workspace, const DispatchPlan& p,
-                           hipStream_t st) {
+                           hipStream_t st, bool counted) {
   uint32_t* table = (uint32_t*)workspace;
-  if (p.nchunks > 0) {
+  if (p.nchunks > 0 && !counted) {  // counted: launch_route_count did it
     const dim3 grid((unsigned)((p.nchunks + p.waves - 1) / p.waves));
     const size_t lds = (size_t)p.waves * (E + 1) * sizeof(uint32_t);
     hipLaunchKernelGGL(dispatch_count_kernel, grid, dim3(64 * p.waves), lds,

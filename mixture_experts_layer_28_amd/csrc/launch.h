@@ -68,7 +68,19 @@ hipError_t launch_dispatch(const void* x, int dt, int64_t T, int64_t H,
                            uint32_t* offsets, uint32_t* row_expert,
                            uint32_t* row_token, uint32_t* token_row,
                            void* workspace, const DispatchPlan& plan,
-                           hipStream_t st);
+                           hipStream_t st, bool counted = false);
+// Softmax routing and the count step of `plan` in one launch (then
+// launch_dispatch with counted = true): where k divides the plan's chunk,
+// E <= kMaxFusedE and a chunk's ids and counters fit kMaxFusedLds u32 of
+// LDS.  Writes idx, w, the count table and the per-chunk ranks exactly as
+// launch_route followed by the count kernel does.
+constexpr int kMaxFusedE = 1024;
+constexpr int64_t kMaxFusedLds = 8192;
+bool route_count_fusable(int E, int k, const DispatchPlan& plan);
+hipError_t launch_route_count(const void* logits, int ldt, int64_t T, int E,
+                              int k, int renorm, uint32_t* idx, void* w,
+                              const DispatchPlan& plan, uint32_t* table,
+                              uint32_t* local_rank, hipStream_t st);
 // The static count table of moe_dispatch_noalloc: its size, and its device
 // address on the current device (looked up once per device, never
 // allocated).

@@ -221,14 +221,17 @@ ForwardLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E,
 
 namespace moe {
 void timing_mark(int n, hipStream_t st) {
-  if (g_in_forward && g_nmarks == MOE_TIMING_EVENTS && n >= 0 && n < g_nmarks)
+  if (g_in_forward && g_nmarks == MOE_TIMING_EVENTS && n >= 0 &&
+      n < g_nmarks && g_marks[n])
     (void)hipEventRecord(g_marks[n], st);
 }
 }  // namespace moe
 
-// The stages after routing, shared by both forwards: the checks that do
+// The stages after routing, shared by the forwards: the checks that do
 // not depend on the routing method, the workspace carve-up and the launch
-// sequence.  `route(idx, w, stream)` launches the routing kernel.
+// sequence.  `route(idx, w, stream, plan, table, rank, &counted)` launches
+// the routing kernel; where it also ran the dispatch count of `plan` into
+// table/rank (one launch instead of two) it sets counted.
 template <typename Route>
 int run_forward(const char* f, const void* x, int dt, int ldt, int64_t T,
                 int64_t H, int64_t I, int64_t E, int64_t top_k,
@@ -269,8 +272,10 @@ int run_forward(const char* f, const void* x, int dt, int ldt, int64_t T,
     Marking() { g_in_forward = true; }
     ~Marking() { g_in_forward = false; }
   } marking;
+  const moe::DispatchPlan plan = moe::plan_dispatch(T, E, top_k);
+  bool counted = false;
   moe::timing_mark(0, st);
-  hipError_t err = route(idx, w, st);
+  hipError_t err = route(idx, w, st, plan, (uint32_t*)dws, token_row, &counted);
   std::snprintf(what, sizeof(what), "%s(route)", f);
   if (err != hipSuccess) return hip_status(err, what);
   // Where the MFMA kernels can read the token rows in place, dispatch
@@ -281,8 +286,7 @@ int run_forward(const char* f, const void* x, int dt, int ldt, int64_t T,
   moe::timing_mark(1, st);
   err = moe::launch_dispatch(x, dt, T, H, (int)E, (int)top_k, idx,
                              gather ? nullptr : xd, offsets, row_expert,
-                             row_token, token_row, dws,
-                             moe::plan_dispatch(T, E, top_k), st);
+                             row_token, token_row, dws, plan, st, counted);
   std::snprintf(what, sizeof(what), "%s(dispatch)", f);
   if (err != hipSuccess) return hip_status(err, what);
   moe::timing_mark(4, st);
@@ -312,10 +316,7 @@ int moe_set_timing_events(void* const* events, int count) {
   }
   if (count != MOE_TIMING_EVENTS || !events)
     return fail(MOE_ERR_INVALID_ARG, "moe_set_timing_events: need %d events", MOE_TIMING_EVENTS);
-  for (int i = 0; i < count; ++i) {
-    if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "moe_set_timing_events: null event");
-    g_marks[i] = (hipEvent_t)events[i];
-  }
+  for (int i = 0; i < count; ++i) g_marks[i] = (hipEvent_t)events[i];  // NULL: mark skipped
   g_nmarks = count;
   return ok();
 }
@@ -475,7 +476,14 @@ int moe_forward(const void* x, int dt, const void* logits, int ldt,
   return run_forward(
       "moe_forward", x, dt, ldt, T, H, I, E, top_k, w_gate, w_up, w_down, out,
       workspace, workspace_bytes, stream,
-      [&](uint32_t* idx, void* w, hipStream_t st) {
+      [&](uint32_t* idx, void* w, hipStream_t st, const moe::DispatchPlan& p,
+          uint32_t* table, uint32_t* rank, bool* counted) {
+        if (moe::route_count_fusable((int)E, (int)top_k, p)) {
+          *counted = true;
+          return moe::launch_route_count(logits, ldt, T, (int)E, (int)top_k,
+                                         renormalize ? 1 : 0, idx, w, p,
+                                         table, rank, st);
+        }
         return moe::launch_route(logits, ldt, T, (int)E, (int)top_k,
                                  renormalize ? 1 : 0, idx, w, st);
       });
@@ -499,7 +507,14 @@ int moe_forward_clipped(const void* x, int dt, const void* logits, int ldt,
   return run_forward(
       "moe_forward_clipped", x, dt, ldt, T, H, I, E, top_k, w_gate, w_up,
       w_down, out, workspace, workspace_bytes, stream,
-      [&](uint32_t* idx, void* w, hipStream_t st) {
+      [&](uint32_t* idx, void* w, hipStream_t st, const moe::DispatchPlan& p,
+          uint32_t* table, uint32_t* rank, bool* counted) {
+        if (moe::route_count_fusable((int)E, (int)top_k, p)) {
+          *counted = true;
+          return moe::launch_route_count(logits, ldt, T, (int)E, (int)top_k,
+                                         renormalize ? 1 : 0, idx, w, p,
+                                         table, rank, st);
+        }
         return moe::launch_route(logits, ldt, T, (int)E, (int)top_k,
                                  renormalize ? 1 : 0, idx, w, st);
       },
@@ -543,7 +558,8 @@ int moe_forward_sigmoid_grouped(const void* x, int dt, const void* logits,
   return run_forward(
       "moe_forward_sigmoid_grouped", x, dt, ldt, T, H, I, E, top_k, w_gate,
       w_up, w_down, out, workspace, workspace_bytes, stream,
-      [&](uint32_t* idx, void* w, hipStream_t st) {
+      [&](uint32_t* idx, void* w, hipStream_t st, const moe::DispatchPlan&,
+          uint32_t*, uint32_t*, bool*) {
         return moe::launch_route_sigmoid(logits, ldt, bias, T, (int)E,
                                          (int)top_k, o, idx, w, st);
       });

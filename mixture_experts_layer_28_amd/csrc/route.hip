@@ -37,7 +37,7 @@ template <int LDT, int G, int PL, bool VEC>
 __device__ __forceinline__ void route_row(
     const typename Storage<LDT>::T* __restrict__ logits, int64_t row, int E,
     int k, int renorm, uint32_t* __restrict__ idx,
-    typename Storage<LDT>::T* __restrict__ w) {
+    typename Storage<LDT>::T* __restrict__ w, uint32_t* keep = nullptr) {
   using S = typename Storage<LDT>::T;
   const int lane = threadIdx.x % G;
   const S* src = logits + row * (int64_t)E + lane * PL;
@@ -74,6 +74,7 @@ __device__ __forceinline__ void route_row(
   if (bad) {
     for (int j = lane; j < k; j += G) {
       idx_row[j] = (uint32_t)j;
+      if (keep) keep[j] = (uint32_t)j;
       w_row[j] = from_f32<LDT>(__builtin_nanf(""));
     }
     return;
@@ -133,6 +134,7 @@ __device__ __forceinline__ void route_row(
     const int j = lane + G * m;
     if (j < k) {
       idx_row[j] = 0xffffffffu - (uint32_t)kj[m];
+      if (keep) keep[j] = 0xffffffffu - (uint32_t)kj[m];
       w_row[j] = from_f32<LDT>(renorm ? pj[m] / den : pj[m]);
     }
   }
@@ -152,6 +154,66 @@ __global__ __launch_bounds__(256) void route_kernel(
   for (int64_t row = (int64_t)blockIdx.x * R + threadIdx.x / G; row < T;
        row += (int64_t)gridDim.x * R)
     route_row<LDT, G, PL, VEC>(logits, row, E, k, renorm, idx, w);
+}
+
+// Routing and the dispatch count in one launch (the forward's first two
+// kernels): workgroup b takes chunk c = b, b + grid, ... of the dispatch
+// plan, whose `chunk` entries are chunk / k whole tokens (k divides the
+// chunk).  Its groups route those tokens as route_kernel does, also keeping
+// the expert ids in LDS; then wavefront 0 counts the chunk exactly as
+// dispatch_count_kernel counts it (same table row, same ranks), reading the
+// ids from LDS.  LDS: chunk ids + E + 1 counters.
+template <int LDT, int G, int PL, bool VEC>
+__global__ __launch_bounds__(256) void route_count_kernel(
+    const typename Storage<LDT>::T* __restrict__ logits, int64_t T, int E,
+    int k, int renorm, uint32_t* __restrict__ idx,
+    typename Storage<LDT>::T* __restrict__ w, int64_t chunk, int64_t nchunks,
+    uint32_t* __restrict__ table, uint32_t* __restrict__ local_rank) {
+  extern __shared__ uint32_t sm[];
+  uint32_t* ids = sm;
+  uint32_t* cnt = sm + chunk;
+  constexpr int R = 256 / G;  // rows per pass of the workgroup
+  const int64_t tpc = chunk / k;
+  const int64_t N = T * (int64_t)k;
+  const int nb = E + 1;
+  const int lane = threadIdx.x % 64;
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int64_t tok0 = c * tpc;
+    for (int64_t r = threadIdx.x / G; r < tpc; r += R) {
+      if (tok0 + r < T)  // uniform across the row's group
+        route_row<LDT, G, PL, VEC>(logits, tok0 + r, E, k, renorm, idx, w,
+                                   ids + r * k);
+    }
+    __syncthreads();  // the chunk's ids are in LDS
+    if (threadIdx.x < 64) {
+      for (int b = lane; b < nb; b += 64) cnt[b] = 0u;
+      const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      const int nbits = 32 - __builtin_clz((unsigned)E | 1u);
+      const int64_t i0 = c * chunk;
+      const int64_t i1 = (i0 + chunk < N) ? i0 + chunk : N;
+      for (int64_t g = i0; g < i1; g += 64) {
+        const int64_t i = g + lane;
+        const bool valid = i < i1;
+        uint32_t e = valid ? ids[i - i0] : 0u;
+        if (e > (uint32_t)E) e = (uint32_t)E;
+        uint64_t same = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+          const uint64_t m = __ballot(valid && ((e >> bit) & 1u));
+          same &= ((e >> bit) & 1u) ? m : ~m;
+        }
+        const int leader = valid ? (int)__builtin_ctzll(same) : lane;
+        uint32_t old = 0;
+        if (valid && leader == lane) {
+          old = cnt[e];
+          cnt[e] = old + (uint32_t)__popcll(same);
+        }
+        old = (uint32_t)__shfl((int)old, leader, 64);
+        if (valid) local_rank[i] = old + (uint32_t)__popcll(same & lt);
+      }
+      for (int b = lane; b < nb; b += 64) table[c * nb + b] = cnt[b];
+    }
+    __syncthreads();  // LDS free for the next chunk
+  }
 }
 
 // Wide rows (E > 1024): one wave per row, values re-read each round; with
@@ -262,7 +324,69 @@ hipError_t launch_route_t(const void* logits, int64_t T, int E, int k,
   return hipGetLastError();
 }
 
+template <int LDT, int G, int PL>
+hipError_t launch_gc(const void* logits, int64_t T, int E, int k, int renorm,
+                     uint32_t* idx, void* w, const DispatchPlan& p,
+                     uint32_t* table, uint32_t* local_rank, hipStream_t st) {
+  using S = typename Storage<LDT>::T;
+  const dim3 grid((unsigned)(p.nchunks < kMaxBlocks ? p.nchunks : kMaxBlocks));
+  const size_t lds = (size_t)(p.chunk + E + 1) * sizeof(uint32_t);
+  const bool vec = (PL * sizeof(S)) % 16 == 0 && E == G * PL &&
+                   (uintptr_t)logits % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL((route_count_kernel<LDT, G, PL, true>), grid, dim3(256),
+                       lds, st, (const S*)logits, T, E, k, renorm, idx, (S*)w,
+                       p.chunk, p.nchunks, table, local_rank);
+  else
+    hipLaunchKernelGGL((route_count_kernel<LDT, G, PL, false>), grid, dim3(256),
+                       lds, st, (const S*)logits, T, E, k, renorm, idx, (S*)w,
+                       p.chunk, p.nchunks, table, local_rank);
+  return hipGetLastError();
+}
+
+template <int LDT>
+hipError_t launch_route_count_t(const void* logits, int64_t T, int E, int k,
+                                int renorm, uint32_t* idx, void* w,
+                                const DispatchPlan& p, uint32_t* table,
+                                uint32_t* rank, hipStream_t st) {
+#define MOE_RC(G, PL) \
+  launch_gc<LDT, G, PL>(logits, T, E, k, renorm, idx, w, p, table, rank, st)
+  if (E <= 8) return MOE_RC(1, 8);
+  if (E <= 16) return MOE_RC(2, 8);
+  if (E <= 32) return MOE_RC(4, 8);
+  if (E <= 64) return MOE_RC(8, 8);
+  if (E <= 128) return MOE_RC(16, 8);
+  if (E <= 256) return MOE_RC(32, 8);
+  if (E <= 512) return MOE_RC(64, 8);
+  return MOE_RC(64, 16);
+#undef MOE_RC
+}
+
 }  // namespace
+
+bool route_count_fusable(int E, int k, const DispatchPlan& p) {
+  if (E < 1 || E > kMaxFusedE || k < 1 || p.nchunks <= 0 ||
+      p.chunk % k != 0 || p.chunk + E + 1 > kMaxFusedLds)
+    return false;
+  // lanes per row as launch_route_count_t picks them; at most 4 passes of
+  // 256 / G rows per chunk (beyond that the separate routing launch, with
+  // a workgroup per 256 / G rows, spreads the rows wider)
+  int G = 1;
+  while (G < 64 && G * 8 < E) G *= 2;
+  return p.chunk / k <= 4 * (256 / G);
+}
+
+hipError_t launch_route_count(const void* logits, int ldt, int64_t T, int E,
+                              int k, int renorm, uint32_t* idx, void* w,
+                              const DispatchPlan& p, uint32_t* table,
+                              uint32_t* local_rank, hipStream_t st) {
+  if (!route_count_fusable(E, k, p)) return hipErrorInvalidValue;
+  switch (ldt) {
+    case DT_F32: return launch_route_count_t<DT_F32>(logits, T, E, k, renorm, idx, w, p, table, local_rank, st);
+    case DT_F16: return launch_route_count_t<DT_F16>(logits, T, E, k, renorm, idx, w, p, table, local_rank, st);
+    default: return launch_route_count_t<DT_BF16>(logits, T, E, k, renorm, idx, w, p, table, local_rank, st);
+  }
+}
 
 hipError_t launch_route(const void* logits, int ldt, int64_t T, int E, int k,
                         int renorm, uint32_t* idx, void* w, hipStream_t st) {

@@ -71,11 +71,23 @@ def test_ragged_shapes(T, H, I, E, k, renorm):
     assert_close(values(out), ref["out"], "bf16", "ragged")
 
 
-def test_staged_equals_one_call():
-    wl = workloads.make("edge", T=300, H=128, I=192)
+# (T, H, I, E, k).  moe_forward routes and counts in one launch where k
+# divides the dispatch chunk (64 entries, doubled while there are more than
+# 256 chunks), E <= 1024 and a chunk's tokens take at most 4 routing passes
+# of its workgroup; the staged calls always launch them apart.  Covered:
+# fused with chunks of 64 to 256 entries, one to four passes, a partial
+# last chunk, E = 1024 (the widest fused route); unfused for k = 3 and 6
+# (k does not divide the chunk), for chunks needing more passes, and for
+# E = 1500 (the wide route).
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (300, 128, 192, 16, 4), (1, 64, 64, 8, 2), (37, 64, 64, 64, 8),
+    (3000, 64, 64, 1024, 8), (4000, 64, 64, 256, 8), (70001, 64, 64, 256, 8),
+    (1000, 64, 64, 7, 3), (513, 64, 64, 40, 6), (200, 64, 64, 1500, 4),
+    (4096, 64, 64, 16, 16)])
+def test_staged_equals_one_call(T, H, I, E, k):
+    wl = workloads.make("edge", T=T, H=H, I=I, E=E)
     wl = {key: (v.to(torch.bfloat16).cuda() if torch.is_tensor(v) else v)
           for key, v in wl.items()}
-    k, E = 4, wl["E"]
     one = moe.moe_forward(wl["x"], wl["logits"], wl["w_gate"], wl["w_up"],
                           wl["w_down"], k, True)
     idx, w = moe.moe_route(wl["logits"], k, True)
@@ -150,6 +162,36 @@ def test_timing_events_bracket_each_kernel():
     torch.cuda.synchronize()
     assert evs[0].elapsed_time(evs[7]) == whole
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_timing_events_null_entries_skip_marks():
+    """Only events[4] and events[5] set (the other entries NULL): the two
+    bracket the gate+up GEMM alone, and the forward's result is unchanged."""
+    import ctypes
+    from mixture_experts_layer_28_amd import _lib
+    wl = workloads.make("edge", device="cuda", k=4)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    stream = torch.cuda.current_stream()
+    for ev in evs:
+        ev.record(stream)
+    torch.cuda.synchronize()
+    before = evs[0].elapsed_time(evs[7])
+    handles = (ctypes.c_void_p * 8)(*[ev.cuda_event if i in (4, 5) else None
+                                      for i, ev in enumerate(evs)])
+    L = _lib.lib()
+    _lib.check(L.moe_set_timing_events(handles, 8))
+    try:
+        out = moe.moe_forward(wl["x"], wl["logits"], wl["w_gate"], wl["w_up"],
+                              wl["w_down"], 4, True)
+    finally:
+        _lib.check(L.moe_set_timing_events(None, 0))
+    torch.cuda.synchronize()
+    assert evs[4].elapsed_time(evs[5]) > 0.0
+    assert evs[0].elapsed_time(evs[7]) == before  # never re-recorded
+    ref = moe.moe_forward(wl["x"], wl["logits"], wl["w_gate"], wl["w_up"],
+                          wl["w_down"], 4, True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
 def test_binding_rejects_mismatched_tensors():
