@@ -191,9 +191,12 @@ TRAFFIC_SOURCES = [
     "mixture_experts_layer_28_amd/csrc/device_common.h",
     "mixture_experts_layer_28_amd/csrc/gemm.hip",
 ]
-# kernel-name fragment of each timed kernel whose traffic is recorded
-TRAFFIC_KERNELS = {"gateup_gemm": "gemm_big_kernel<2, true",
-                   "down_gemm": "gemm_big_kernel<2, false"}
+# kernel-name fragments of each timed kernel whose traffic is recorded
+# (prefill and decode-sized forms)
+TRAFFIC_KERNELS = {"gateup_gemm": ("gemm_big_kernel<2, true",
+                                   "gemm_mfma_kernel<2, 32, 128, 1, true"),
+                   "down_gemm": ("gemm_big_kernel<2, false",
+                                 "gemm_mfma_kernel<2, 32, 128, 1, false")}
 
 
 def _counter_rows(run_dir):
@@ -256,9 +259,11 @@ def record_traffic(workload, prof_dir, copy_dir):
     sha = _sources_sha256()
     lines = ["| kernel | FETCH_SIZE KiB per dispatch | WRITE_SIZE KiB per "
              "dispatch | scaled traffic per launch |", "|---|---|---|---|"]
-    for key, frag in TRAFFIC_KERNELS.items():
-        fk = [v for d, (n, v) in sorted(fetch.items()) if frag in n]
-        wk = [v for d, (n, v) in sorted(write.items()) if frag in n]
+    for key, frags in TRAFFIC_KERNELS.items():
+        fk = [v for d, (n, v) in sorted(fetch.items())
+              if any(f in n for f in frags)]
+        wk = [v for d, (n, v) in sorted(write.items())
+              if any(f in n for f in frags)]
         if not fk or not wk:
             continue
         traffic = int(round(sum(fk) / len(fk) * 1024 * fetch_factor +
