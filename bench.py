@@ -38,9 +38,21 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # The forward's stages between its timing marks.  Its dispatch writes only
-# the mapping (dispatch_map): the gate+up GEMM gathers the token rows from x.
-KERNELS = ["route", "dispatch_count", "dispatch_scan", "dispatch_map",
+# the mapping where the gate+up GEMM gathers the token rows from x, else it
+# also scatters them (forward_gathers).
+KERNELS = ["route", "dispatch_count", "dispatch_scan", "dispatch",
            "gateup_gemm", "down_gemm", "combine"]
+
+
+def forward_gathers(wl):
+    """Whether moe_forward reads the token rows in place for this workload
+    (the library's rule: the MFMA paths, except prefill-sized segments with
+    more than 32 gate+up column blocks of 256, where the scatter is cheaper)."""
+    N, E, I = wl["T"] * wl["k"], wl["E"], wl["I"]
+    if wl["fmt"] == "f32":
+        return False
+    prefill = N >= 96 * E
+    return not (prefill and 2 * I > 32 * 256)
 
 
 def mark_cost_ms(dev):
@@ -174,8 +186,10 @@ def algorithmic(wl, counts):
                       + (E * 4 if wl.get("bias") is not None else 0)),
         "dispatch_count": dict(bytes=N * 4 * 2),
         "dispatch_scan": dict(bytes=(E + 1) * 4),
-        # idx and ranks read, token_row / row_expert / row_token written
-        "dispatch_map": dict(bytes=N * 4 * 5),
+        # idx and ranks read, token_row / row_expert / row_token written;
+        # with the scatter also every token row read and its k copies written
+        "dispatch": dict(bytes=N * 4 * 5 + (0 if forward_gathers(wl)
+                                            else T * H * s + N * H * s)),
         "gateup_gemm": dict(flop=4 * N * H * I,
                             bytes=N * H * s + w_gu + N * I * s),
         "down_gemm": dict(flop=2 * N * H * I,

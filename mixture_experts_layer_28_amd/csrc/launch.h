@@ -111,9 +111,10 @@ hipError_t launch_experts(const void* xd, int dt, int64_t N, int64_t H,
                           const uint32_t* offsets, void* act, void* y,
                           hipStream_t st, Swiglu sw = Swiglu{},
                           Gather ga = Gather{});
-// Whether launch_experts can take its A rows through a Gather for these
-// sizes and pointers (the MFMA paths, with x [xrows, H] addressable by
-// 32-bit byte offsets); otherwise xd must be materialised.
+// Whether launch_experts takes its A rows through a Gather for these sizes
+// and pointers (the MFMA paths, with x [xrows, H] addressable by 32-bit
+// byte offsets, and for prefill-sized segments at most kGatherMaxColBlocks
+// gate+up column blocks); otherwise xd is materialised.
 bool experts_can_gather(int dt, int64_t N, int64_t H, int64_t I, int E,
                         int64_t xrows, const void* x, const void* w_gate,
                         const void* w_up, const void* w_down, const void* act,
