@@ -332,14 +332,18 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 
   const int wid = uniform(tid >> 6) & 7, lane = tid & 63;
   const int wm = wid / WN, wn = wid % WN;
-  // B rows in LDS.  The plain products read B rows 8 apart in one
-  // fragment (brow0 below), so B row r = 64a + 8b + c is kept at LDS row
-  // 64a + 8c + b: a fragment read then covers 8 consecutive LDS rows, whose
-  // chunks rotate by LDS row like A's (rotating rows 8 apart by row / 8
-  // instead left bank conflicts).  The gate+up product reads consecutive
-  // rows and keeps them in order.
-  auto bsrc = [](int R) {  // B tile row held at LDS row R (an involution)
-    return GATEUP ? R : (R & ~63) | ((R & 7) << 3) | ((R >> 3) & 7);
+  // B rows in LDS, permuted so that each lane's MFMA columns are
+  // consecutive output columns while every fragment read still covers
+  // consecutive LDS rows (their chunks rotate by LDS row like A's).  Plain
+  // products: a lane's 8 columns are 8 consecutive outputs, so B row
+  // r = 64a + 8b + c is kept at LDS row 64a + 8c + b (rotating rows 8
+  // apart by row / 8 instead left bank conflicts).  Gate+up: a lane's 4
+  // gate columns, and the 4 up columns paired with them, are 4 consecutive
+  // act columns, so gate (or up) row r = 64a + 4n + j is kept at LDS row
+  // 64a + 16j + n.
+  auto bsrc = [](int R) {  // B tile row held at LDS row R
+    return GATEUP ? (R & ~63) | ((R & 15) << 2) | ((R >> 4) & 3)
+                  : (R & ~63) | ((R & 7) << 3) | ((R >> 3) & 7);
   };
 
   // MFMA row tiles of this wave: t16 tiles over 4 wave rows, the first
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         const int R = 8 * bb + (lane >> 3);
         const int kk = k0 + ((lane & 7) ^ swz(R)) * 8;
         const bool up = GATEUP && (j - AJ) * 64 >= kBN / 2;  // rows >= 128
-        const int br = up ? R - kBN / 2 : bsrc(R);
+        const int br = up ? bsrc(R) - kBN / 2 : bsrc(R);
         uint32_t bo = kk < K ? (uint32_t)(boff + br) * rowbytes + kk * (uint32_t)sizeof(S) : OOB;
         // an opaque copy of the offset: without it the compiler turned the
         // K-tail select into a branch around the last B loads, which cut
@@ -402,12 +406,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   // Plain products: column j of a lane is output column (lane % 16) * 8 + j
   // of the wave's 128, so after the K loop each lane holds 8 consecutive
   // outputs of a row and the epilogue stores them as one 16-byte vector.
-  // Gate+up: column j < 4 is gate column 16 j + lane % 16 of the wave's 64
-  // act columns and j >= 4 the up column of the same act column (this
-  // product keeps consecutive rows per fragment: the permuted form cost it
-  // registers and spills).
+  // Gate+up: column j < 4 is gate column (lane % 16) * 4 + j of the wave's
+  // 64 act columns and j >= 4 the up column of the same act column, so each
+  // lane holds 4 consecutive act outputs of a row.
   // (Plain products: B row wn * 128 + (lane % 16) * 8 + j sits at LDS row
-  // wn * 128 + 64 * ((lane / 8) % 2) + 8 j + lane % 8.)
+  // wn * 128 + 64 * ((lane / 8) % 2) + 8 j + lane % 8; gate+up: gate row
+  // wn * 64 + (lane % 16) * 4 + j at LDS row wn * 64 + 16 j + lane % 16.)
   const int brow0 = GATEUP ? wn * (TN / 2) + (lane & 15)
                            : wn * TN + ((lane >> 3) & 1) * 64 + (lane & 7);
   auto bstep = [](int j) -> int {
@@ -609,15 +613,22 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         }
         S* crow = C + r * NB;
         if (GATEUP) {
+          // act columns 4 (lane % 16) .. + 3 of the wave's 64: one 8-byte
+          // store (they were 16 apart, four 2-byte stores: the epilogue
+          // took 14 % of a Mixtral-shaped gate+up tile)
           constexpr int H2 = FN / 2;
+          const int64_t c0 = n0 + wn * (TN / 2) + (lane & 15) * H2;
+          if (c0 < NB) {
+            S v[H2];
 #pragma unroll
-          for (int j = 0; j < H2; ++j) {
-            const int64_t c = n0 + wn * (TN / 2) + j * 16 + (lane & 15);
-            if (c < NB) {
+            for (int j = 0; j < H2; ++j) {
               const float g = to_f32<D>(from_f32<D>(acc[i][j][q]));
               const float u = to_f32<D>(from_f32<D>(acc[i][j + H2][q]));
-              crow[c] = from_f32<D>(swiglu_act(g, u, sw));
+              v[j] = from_f32<D>(swiglu_act(g, u, sw));
             }
+            u32x2 pk;
+            __builtin_memcpy(&pk, v, sizeof(pk));
+            *(u32x2*)(crow + c0) = pk;
           }
         } else {
           const int64_t c0 = n0 + wn * TN + (lane & 15) * FN;
