@@ -454,9 +454,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
           acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
     };
     dma(0, 0);
-    wait_vmem();
-    __syncthreads();
-    if (nk > 1) dma(kBK, 1);
+    if (nk > 1) {
+      // both first stages in flight before the first wait, so stage 1's
+      // latency overlaps stage 0's; a raw barrier, because __syncthreads'
+      // release fence would wait for stage 1 as well
+      dma(kBK, 1);
+      static_assert(BLK == 9, "the count below leaves one stage in flight");
+      asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
+    } else {
+      wait_vmem();
+      __syncthreads();
+    }
     if constexpr (FMC > 0 && FMC <= 4) {
       // The second half of stage kt is multiplied after the barrier, while
       // the first half of stage kt+1 is read from LDS into the other

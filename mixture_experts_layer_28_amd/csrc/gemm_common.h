@@ -53,15 +53,16 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 // segment of R rows has ceil(R / BM) row blocks: of BM rows each (the last
 // one shorter) or, with `balanced`, made of the ceil(R / 32) units of 32
 // rows (the last unit partial) dealt out as evenly as possible, so that no
-// row block is a thin remainder (BM a multiple of 32).  Pass 1 totals the
-// real tiles; they are then dealt to the 8 XCDs (hardware deals workgroup b
-// to XCD b % 8) in chunks of kXcdChunk consecutive logical tiles, round
-// robin: the tiles of one chunk run side by side on one XCD and share its
-// L2, and every XCD gets a mix of large and small tiles.  (Contiguous
-// ranges of equal tile counts per XCD left the XCD holding the most large
-// tiles of a skewed routing ~9 % above the mean; the fine-grained expert
-// stage ran 7 % faster with chunks of 16.)  Pass 2 finds the segment of
-// logical tile L.  Inside a segment, tiles go in groups of up to 8 row
+// row block is a thin remainder (BM a multiple of 32).  The logical tiles
+// are dealt to the 8 XCDs (hardware deals workgroup b to XCD b % 8) in
+// chunks of kXcdChunk consecutive logical tiles, round robin: the tiles of
+// one chunk run side by side on one XCD and share its L2, and every XCD
+// gets a mix of large and small tiles.  (Contiguous ranges of equal tile
+// counts per XCD left the XCD holding the most large tiles of a skewed
+// routing ~9 % above the mean; the fine-grained expert stage ran 7 %
+// faster with chunks of 16.)  One pass over the segments (a wave prefix
+// sum of their tile counts) finds the segment of workgroup b's logical
+// tile L.  Inside a segment, tiles go in groups of up to 8 row
 // blocks: all column blocks of a group before the next group, the row
 // blocks of one column block consecutive.
 // G must be at least tile_grid(tiles).
@@ -72,16 +73,10 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
                                    bool balanced = false) {
   const int lane = threadIdx.x;
   if (lane == 0) ti->found = 0;
-  uint32_t total = 0;
-  for (int s0 = 0; s0 < nseg; s0 += 64) {
-    int64_t lo, hi;
-    segment(offsets, s0 + lane, E, N, nseg, &lo, &hi);
-    const uint32_t cnt = (uint32_t)((hi - lo + BM - 1) / BM) * ncol;
-    total += __shfl(wave_inclusive_sum(cnt, lane), 63, 64);
-  }
+  // the deal does not depend on the total: one pass over the segments
+  // finds logical tile L, and an L past the last tile finds none
   const uint32_t local = b / 8u, q = local / kXcdChunk;
   const uint32_t L = (q * 8u + b % 8u) * kXcdChunk + local % kXcdChunk;
-  if (L >= total) return;
   (void)G;
   uint32_t base = 0;
   for (int s0 = 0; s0 < nseg; s0 += 64) {
