@@ -51,9 +51,10 @@ namespace {
 // lanes: the kernel then keeps no tile record in LDS and needs no barrier
 // before its K loop, so four of its workgroups fit the 160 KB of LDS of a
 // CU (the record pushed each one just past a quarter).
+template <int BM>
 __device__ inline TileInfo locate_tile_wave(uint32_t b,
                                             const uint32_t* __restrict__ offsets,
-                                            int E, int64_t N, int BM,
+                                            int E, int64_t N,
                                             uint32_t ncol, int nseg) {
   const int lane = threadIdx.x & 63;
   TileInfo t;
@@ -64,7 +65,8 @@ __device__ inline TileInfo locate_tile_wave(uint32_t b,
   for (int s0 = 0; s0 < nseg; s0 += 64) {
     int64_t lo, hi;
     segment(offsets, s0 + lane, E, N, nseg, &lo, &hi);
-    const uint32_t cnt = (uint32_t)((hi - lo + BM - 1) / BM) * ncol;
+    const uint32_t R32 = (uint32_t)(hi - lo);  // N < 2^32
+    const uint32_t cnt = (R32 / BM + (R32 % BM != 0)) * ncol;
     total += __shfl(wave_inclusive_sum(cnt, lane), 63, 64);
   }
   const uint32_t per = (total + 7u) / 8u, local = b / 8u;
@@ -74,7 +76,8 @@ __device__ inline TileInfo locate_tile_wave(uint32_t b,
   for (int s0 = 0; s0 < nseg; s0 += 64) {
     int64_t lo, hi;
     segment(offsets, s0 + lane, E, N, nseg, &lo, &hi);
-    const uint32_t nt = (uint32_t)((hi - lo + BM - 1) / BM);
+    const uint32_t R32 = (uint32_t)(hi - lo);
+    const uint32_t nt = R32 / BM + (R32 % BM != 0);
     const uint32_t cnt = nt * ncol;
     const uint32_t inc = wave_inclusive_sum(cnt, lane);
     const uint32_t exc = inc - cnt;
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 
   const int tid = threadIdx.x;
   const TileInfo ti =
-      locate_tile_wave(blockIdx.x, offsets, E, N, BM, ncol, nseg);
+      locate_tile_wave<BM>(blockIdx.x, offsets, E, N, ncol, nseg);
   if (!ti.found) return;  // the same answer in every wavefront
   const int e = uniform(ti.e);
   const int64_t hi = uniform(ti.hi), row0 = uniform(ti.row0);
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
   __shared__ TileInfo ti;
   const int tid = threadIdx.x;
   if (tid < 64)
-    locate_tile(blockIdx.x, gridDim.x, offsets, E, N, BM, ncol, nseg, &ti);
+    locate_tile<BM>(blockIdx.x, gridDim.x, offsets, E, N, ncol, nseg, &ti);
   __syncthreads();
   if (!ti.found) return;
   const int e = uniform(ti.e);

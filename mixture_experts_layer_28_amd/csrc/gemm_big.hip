@@ -288,7 +288,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     }
   } else {
     if (tid < 64)
-      locate_tile(blockIdx.x, gridDim.x, offsets, E, N, kBM, ncol, nseg, &ti,
+      locate_tile<kBM>(blockIdx.x, gridDim.x, offsets, E, N, ncol, nseg, &ti,
                   true);
     __syncthreads();
     if (!ti.found) return;

@@ -65,10 +65,13 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 // tile L.  Inside a segment, tiles go in groups of up to 8 row
 // blocks: all column blocks of a group before the next group, the row
 // blocks of one column block consecutive.
-// G must be at least tile_grid(tiles).
+// G must be at least tile_grid(tiles).  BM is a template argument so that
+// the per-segment block counts divide by a constant (a 64-bit division by
+// a runtime value is a long instruction sequence).
+template <int BM>
 __device__ inline void locate_tile(uint32_t b, uint32_t G,
                                    const uint32_t* __restrict__ offsets,
-                                   int E, int64_t N, int BM, uint32_t ncol,
+                                   int E, int64_t N, uint32_t ncol,
                                    int nseg, TileInfo* ti,
                                    bool balanced = false) {
   const int lane = threadIdx.x;
@@ -83,7 +86,8 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
     const int s = s0 + lane;
     int64_t lo, hi;
     segment(offsets, s, E, N, nseg, &lo, &hi);
-    const uint32_t nt = (uint32_t)((hi - lo + BM - 1) / BM);
+    const uint32_t R32 = (uint32_t)(hi - lo);  // N < 2^32
+    const uint32_t nt = R32 / BM + (R32 % BM != 0);
     const uint32_t cnt = nt * ncol;
     const uint32_t inc = wave_inclusive_sum(cnt, lane);
     const uint32_t exc = inc - cnt;
