@@ -374,13 +374,23 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     // up rows, is fixed per unrolled slot (wid < 8), so the issue is
     // straight-line code (it was a chain of uniform branches per block)
     constexpr int AJ = ABLK / 8;  // A blocks per wave: wave w takes w + 8 j
+    // Gathering: the wave's A row offsets, read together (one LDS round
+    // trip before the loads instead of one per load; volatile so the
+    // compiler keeps them out of registers between K steps: held there they
+    // spilled); fine-grained forward 1 % faster.
+    uint32_t ao[AJ];
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int j = 0; j < AJ; ++j)
+        ao[j] = *(volatile uint32_t*)&arow_off[8 * (wid + 8 * j) + (lane >> 3)];
+    }
 #pragma unroll
     for (int j = 0; j < BLK; ++j) {
       if (j < AJ) {
         const int b = wid + 8 * j;  // A block; rows past the tile read zeros
         const int r = 8 * b + (lane >> 3);
         const int kk = k0 + ((lane & 7) ^ swz(r)) * 8;
-        const uint32_t ro = GATHER ? arow_off[r] : (uint32_t)r * rowbytes;
+        const uint32_t ro = GATHER ? ao[j] : (uint32_t)r * rowbytes;
         buffer_load_lds16(rA, base + b * 512,
                           kk < K ? ro + kk * (uint32_t)sizeof(S) : OOB);
       } else {
