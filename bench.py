@@ -559,7 +559,10 @@ def vendor_reference_bench(args):
     of 2I columns) and act_e . W_down_e^T, weights pre-transposed to
     contiguous [K, N] outside the timed region; no SwiGLU (GEMMs only), so
     the library's gate+up epilogue is extra work on its side.  Both run in
-    one process, alternating, torch events around each."""
+    one process, alternating, torch events around each.  A third line runs
+    the same FLOPs ungrouped (all rows against the first expert's weights,
+    two dense products): what the library reaches on a plain GEMM of that
+    size, for scale."""
     import statistics
     import torch
 
@@ -589,11 +592,18 @@ def vendor_reference_bench(args):
             torch.mm(xd[lo:hi], wg, out=gu[lo:hi])
             torch.mm(act[lo:hi], wd, out=yv[lo:hi])
 
+    def vendor_dense():
+        # the same FLOPs with no grouping: every row against one expert's
+        # weights, two dense products (the library's best case)
+        torch.mm(xd, wgu_t[0], out=gu)
+        torch.mm(act, wd_t[0], out=yv)
+
     calls = {
         "library": lambda: moe.moe_experts_forward(
             xd, d["offsets"], wl["w_gate"], wl["w_up"], wl["w_down"],
             act=act, y=y),
         "hipblaslt_per_expert": vendor,
+        "hipblaslt_dense_one_expert": vendor_dense,
     }
     times = {name: [] for name in calls}
     for _ in range(args.warmup):
