@@ -184,7 +184,15 @@ def expert_rows(xd, e, w_gate, w_up, w_down, fmt, clip=None):
     product is an exact float64 matrix product rounded once; gate, up and act
     are rounded to ``fmt`` as the experts page stores them (R-Prec).
     """
-    return round_to(expert_act(xd, w_gate, w_up, fmt, clip) @ w_down.T, fmt)
+    return expert_down(expert_act(xd, w_gate, w_up, fmt, clip), w_down, fmt)
+
+
+def expert_down(act, w_down, fmt):
+    """The down product of one expert's activation rows: act [n,I] times the
+    transpose of its [H,I] down weight, an exact float64 sum rounded once to
+    ``fmt`` (R-Prec).  Output columns are independent, so a slice of the
+    weight's rows gives the matching slice of the columns."""
+    return round_to(act @ w_down.T, fmt)
 
 
 def expert_act(xd, w_gate, w_up, fmt, clip=None):
@@ -228,7 +236,7 @@ def experts(xd, offsets, w_gate, w_up, w_down, fmt, rows=None, clip=None,
         assert wg.shape == (I, H) and wd.shape == (H, I)
         a = expert_act(xd[want[sel]], wg, wu, fmt, clip)
         act[sel] = a
-        out[sel] = round_to(a @ wd.T, fmt)
+        out[sel] = expert_down(a, wd, fmt)
     return (out, act) if with_act else out
 
 

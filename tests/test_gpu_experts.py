@@ -11,7 +11,8 @@ import torch
 import mixture_experts_layer_28_amd as moe
 from mixture_experts_layer_28_amd import workloads
 from oracle.fp import encode_bits, round_to
-from oracle.moe import combine, dispatch, experts, route
+from oracle.moe import (combine, dispatch, expert_act, expert_down, experts,
+                        route)
 from parity_util import assert_close, values
 
 pytestmark = pytest.mark.gpu
@@ -284,3 +285,50 @@ def test_experts_full_size(name, T, every_row):
                  "%s T=%d act, %d rows" % (name, T, len(rows)))
     assert_close(values(y[sel]), y_ref, fmt,
                  "%s T=%d y, %d rows" % (name, T, len(rows)))
+
+
+def test_experts_two_gib_weights():
+    """One expert whose weight matrices reach 2^31 bytes (H = 2048,
+    I = 524288: 2 GiB each) takes the 128 x 128-tile MFMA kernel, because
+    the 320-row kernel addresses a weight matrix with 31-bit buffer
+    offsets; 128 rows, so the prefill regime (N >= 96 E).  act and y of 16
+    rows (the first and the last among them) against the oracle, every
+    column.  The oracle runs on slices of weight rows: an act column
+    depends only on its own gate and up rows, a y column only on its own
+    down row.  The weights are drawn on the device from a seeded torch
+    generator."""
+    fmt, H, I, E, N = "bf16", 2048, 524288, 1, 128
+    assert H * I * 2 >= 2 ** 31
+    print("case: experts with 2 GiB weight matrices", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(2 ** 31)
+    x = torch.randn(N, H, generator=gen, device="cuda", dtype=torch.bfloat16)
+    w = {}
+    for key, shape, fan in (("w_gate", (E, I, H), H), ("w_up", (E, I, H), H),
+                            ("w_down", (E, H, I), I)):
+        w[key] = torch.randn(shape, generator=gen, device="cuda",
+                             dtype=torch.bfloat16).mul_(fan ** -0.5)
+    offsets = _u32(np.array([0, N])).cuda()
+    act = torch.empty((N, I), dtype=torch.bfloat16, device="cuda")
+    y = moe.moe_experts_forward(x, offsets, w["w_gate"], w["w_up"],
+                                w["w_down"], act=act)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, N - 1],
+                                     rng.choice(np.arange(1, N - 1), 14,
+                                                replace=False)]))
+    sel = torch.from_numpy(rows).cuda()
+    xr = values(x[sel])
+    act_ref = np.zeros((len(rows), I))
+    step = 1 << 16
+    for c0 in range(0, I, step):
+        act_ref[:, c0:c0 + step] = expert_act(
+            xr, values(w["w_gate"][0, c0:c0 + step]),
+            values(w["w_up"][0, c0:c0 + step]), fmt)
+    assert_close(values(act[sel]), act_ref, fmt, "act, 2 GiB weights")
+    y_ref = np.zeros((len(rows), H))
+    step = 256
+    for h0 in range(0, H, step):
+        y_ref[:, h0:h0 + step] = expert_down(
+            act_ref, values(w["w_down"][0, h0:h0 + step]), fmt)
+    assert_close(values(y[sel]), y_ref, fmt, "y, 2 GiB weights")
