@@ -708,7 +708,8 @@ def summarize_trace(trace_dir):
                     float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
 
 
-SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs each
+CUS = 256        # MI355X: 256 compute units
+SIMDS = CUS * 4  # ... of 4 SIMDs each
 XCDS = 8         # ... in 8 XCDs
 
 
@@ -752,6 +753,8 @@ def summarize_counters(run_dir):
         derived += ["bf16 MFMA TFLOP", "TFLOP/s"]
     if "GRBM_GUI_ACTIVE" in counters:
         derived.append("GHz")
+    if {"SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"} <= set(counters):
+        derived.append("LDS busy %")
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         if c in counters:
             derived.append(c + " MB")
@@ -777,6 +780,11 @@ def summarize_counters(run_dir):
             row += ["%.4g" % (fl / 1e12), "%.0f" % (fl / (us * 1e-6) / 1e12)]
         if "GHz" in derived:
             row.append("%.2f" % (mean["GRBM_GUI_ACTIVE"] / XCDS / (us * 1e3)))
+        if "LDS busy %" in derived:
+            # cycles a CU's LDS serves indexed (ds_*) accesses, summed over
+            # the CUs, over the active cycles times the CUs
+            row.append("%.1f" % (100.0 * mean.get("SQ_LDS_IDX_ACTIVE", 0)
+                                 / (mean["GRBM_GUI_ACTIVE"] / XCDS * CUS)))
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             if c + " MB" in derived:
                 row.append("%.1f" % (mean.get(c, 0) * 1024 / 1e6))
