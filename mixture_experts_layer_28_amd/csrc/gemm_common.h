@@ -68,12 +68,23 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 // G must be at least tile_grid(tiles).  BM is a template argument so that
 // the per-segment block counts divide by a constant (a 64-bit division by
 // a runtime value is a long instruction sequence).
+//
+// With `split` > 0 (balanced blocks only), a segment whose ceil(R / BM)
+// blocks would average more than `split` units is cut into ceil(units / 8)
+// blocks instead, of at most 8 units (256 rows): then G must be at least
+// tile_grid_chunked over ceil(N / 256) + segments row blocks.
+__device__ __forceinline__ uint32_t row_blocks(uint32_t R32, uint32_t nt,
+                                               int split) {
+  const uint32_t u = (R32 + 31u) / 32u;
+  return split > 0 && u > (uint32_t)split * nt ? (u + 7u) / 8u : nt;
+}
+
 template <int BM>
 __device__ inline void locate_tile(uint32_t b, uint32_t G,
                                    const uint32_t* __restrict__ offsets,
                                    int E, int64_t N, uint32_t ncol,
                                    int nseg, TileInfo* ti,
-                                   bool balanced = false) {
+                                   bool balanced = false, int split = 0) {
   const int lane = threadIdx.x;
   if (lane == 0) ti->found = 0;
   // the deal does not depend on the total: one pass over the segments
@@ -87,7 +98,8 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
     int64_t lo, hi;
     segment(offsets, s, E, N, nseg, &lo, &hi);
     const uint32_t R32 = (uint32_t)(hi - lo);  // N < 2^32
-    const uint32_t nt = R32 / BM + (R32 % BM != 0);
+    const uint32_t nt =
+        row_blocks(R32, R32 / BM + (R32 % BM != 0), balanced ? split : 0);
     const uint32_t cnt = nt * ncol;
     const uint32_t inc = wave_inclusive_sum(cnt, lane);
     const uint32_t exc = inc - cnt;

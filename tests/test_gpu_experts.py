@@ -102,13 +102,16 @@ def test_experts_stage(T, H, I, E, k, fmt, skew):
     _check_stage(d, wg, wu, wd, fmt, "experts %s" % ((T, H, I, E, k, fmt),))
 
 
-@pytest.mark.parametrize("R", [321, 639, 641, 1035, 1065, 1281])
+@pytest.mark.parametrize("R", [300, 321, 639, 641, 1035, 1065, 1281, 2885])
 def test_balanced_row_blocks(R):
     """A prefill segment of R rows is cut into ceil(R / 320) row blocks made
-    of whole 32-row units (the last one partial) dealt out evenly; sizes
-    just past a multiple of the block limit, and 1035 and 1065 rows (blocks
-    of 256-288 rows: 16 to 18 MFMA row tiles, shared 5-5-4-4 at most over
-    the wave rows), must compute every row exactly once."""
+    of whole 32-row units (the last one partial) dealt out evenly, or, where
+    those blocks would average more than 9 units, into blocks of at most 8
+    units (300 rows: 2 blocks instead of 1; 639: 3 instead of 2; 2885: 12
+    instead of 10); sizes just past a multiple of the block limit, and 1035
+    and 1065 rows (blocks of 256-288 rows: 16 to 18 MFMA row tiles, shared
+    5-5-4-4 at most over the wave rows), must compute every row exactly
+    once."""
     rng = np.random.default_rng(R)
     fmt, H, I, E = "bf16", 128, 192, 2
     T = R + 150
