@@ -55,7 +55,7 @@ constexpr int kBM = 320, kBN = 256, kBK = 64;
 // same-process A/B at that shape: the down GEMM ~5 % faster and the
 // forward 2.2 %; the Mixtral shape (blocks of 256-288 rows) unchanged.
 // The gate+up product reading token rows in place keeps 320-row blocks
-// (with the split that launch was 4 % slower).
+// (with the split that launch was 2-4 % slower).
 constexpr int kSplitUnits = 9;
 constexpr int kFM = kBM / 4 / 16;                 // MFMA row tiles per wave, at most
 constexpr int kStage = (kBM + kBN) * kBK;         // elements of one LDS stage
@@ -388,12 +388,16 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     // Gathering: the wave's A row offsets, read together (one LDS round
     // trip before the loads instead of one per load; volatile so the
     // compiler keeps them out of registers between K steps: held there they
-    // spilled); fine-grained forward 1 % faster.
+    // spilled).  The pointer keeps the LDS address space: a volatile read
+    // through a generic pointer is a flat load with the coherence bits set,
+    // which waits on the vector-memory counter too and holds a 64-bit
+    // address per read (fine-grained forward 3 % faster as LDS reads).
     uint32_t ao[AJ];
     if constexpr (GATHER) {
+      typedef volatile __attribute__((address_space(3))) uint32_t lds_u32;
 #pragma unroll
       for (int j = 0; j < AJ; ++j)
-        ao[j] = *(volatile uint32_t*)&arow_off[8 * (wid + 8 * j) + (lane >> 3)];
+        ao[j] = ((lds_u32*)arow_off)[8 * (wid + 8 * j) + (lane >> 3)];
     }
 #pragma unroll
     for (int j = 0; j < BLK; ++j) {
