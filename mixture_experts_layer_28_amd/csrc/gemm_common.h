@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 // tile_grid_chunked over ceil(N / 256) + segments row blocks.
 __device__ __forceinline__ uint32_t row_blocks(uint32_t R32, uint32_t nt,
                                                int split) {
-  const uint32_t u = (R32 + 31u) / 32u;
+  const uint32_t u = R32 / 32u + (R32 % 32u != 0);  // no wrap near 2^32
   return split > 0 && u > (uint32_t)split * nt ? (u + 7u) / 8u : nt;
 }
 
