@@ -98,7 +98,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void* p,
   return make_rsrc((const void*)(uintptr_t)u, (uint64_t)uniform((int64_t)bytes));
 }
 
-template <int D, bool GATEUP, bool GATHER>
+template <int D, bool GATEUP, bool GATHER, bool CLIP>
 __device__ __forceinline__ void tiny_tile(
     const typename Storage<D>::T* A, const typename Storage<D>::T* B0,
     const typename Storage<D>::T* B1, typename Storage<D>::T* C,
@@ -207,7 +207,7 @@ __device__ __forceinline__ void tiny_tile(
         if (c < NB) {
           const float g = to_f32<D>(from_f32<D>(acc[i][0][q]));
           const float u = to_f32<D>(from_f32<D>(acc[i][1][q]));
-          crow[c] = from_f32<D>(swiglu_act(g, u, sw));
+          crow[c] = from_f32<D>(swiglu_act_t<CLIP>(g, u, sw));
         }
       } else {
 #pragma unroll
@@ -231,7 +231,9 @@ __device__ __forceinline__ void tiny_tile(
 // in `K`.
 // GATHER (gate+up only): A row r of the segments is row ga.rows[r] of the
 // token rows x = A [ga.xrows, K] instead of row r of the dispatched copy.
-template <int D, bool GATEUP, bool WG = false, bool GATHER = false>
+// CLIP: the clipped SwiGLU activation (gate+up only).
+template <int D, bool GATEUP, bool WG = false, bool GATHER = false,
+          bool CLIP = false>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const typename Storage<D>::T* __restrict__ A,
     const typename Storage<D>::T* __restrict__ B0,
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     return;
   }
   if (!WG && arows <= kTinyRows) {
-    tiny_tile<D, GATEUP, GATHER>(A, B0, B1, C, ga.rows, ga.xrows, row0,
+    tiny_tile<D, GATEUP, GATHER, CLIP>(A, B0, B1, C, ga.rows, ga.xrows, row0,
                                  arows, n0, e, K, NB, sw);
     return;
   }
@@ -657,7 +659,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
             for (int j = 0; j < H2; ++j) {
               const float g = to_f32<D>(from_f32<D>(acc[i][j][q]));
               const float u = to_f32<D>(from_f32<D>(acc[i][j + H2][q]));
-              v[j] = from_f32<D>(swiglu_act(g, u, sw));
+              v[j] = from_f32<D>(swiglu_act_t<CLIP>(g, u, sw));
             }
             u32x2 pk;
             __builtin_memcpy(&pk, v, sizeof(pk));
@@ -697,25 +699,28 @@ hipError_t launch_one(const void* A, const void* B0, const void* B1, void* C,
   // sum over segments of the row blocks <= ceil(N / block) + nseg
   const uint32_t grid = tile_grid_chunked(
       ncol * (cdiv(N, split > 0 ? 256 : kBM) + (uint32_t)nseg));
-  if (GATEUP && ga.rows) {
+  // one instantiation per (gathering, activation) pair
+  auto go = [&](auto gather_c, auto clip_c) -> hipError_t {
+    constexpr bool G = decltype(gather_c)::value, CL = decltype(clip_c)::value;
     static std::atomic<uint64_t> attr{0};
     hipError_t err = allow_lds(
-        (const void*)gemm_big_kernel<D, GATEUP, false, GATEUP>, attr);
+        (const void*)gemm_big_kernel<D, GATEUP, false, G, CL>, attr);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP, false, GATEUP>),
-                       dim3(grid), dim3(512), kLds, st, (const S*)A,
-                       (const S*)B0, (const S*)B1, (S*)C, offsets, N, K, NB,
-                       E, ncol, nseg, nullptr, sw, ga, split);
+    hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP, false, G, CL>), dim3(grid),
+                       dim3(512), kLds, st, (const S*)A, (const S*)B0,
+                       (const S*)B1, (S*)C, offsets, N, K, NB, E, ncol, nseg,
+                       nullptr, sw, G ? ga : Gather{}, split);
     return hipGetLastError();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if constexpr (GATEUP) {
+    const bool clip = sw.limit >= 0.0f;
+    if (ga.rows) return clip ? go(T{}, T{}) : go(T{}, F{});
+    return clip ? go(F{}, T{}) : go(F{}, F{});
+  } else {
+    return go(F{}, F{});
   }
-  static std::atomic<uint64_t> attr{0};
-  hipError_t err = allow_lds((const void*)gemm_big_kernel<D, GATEUP>, attr);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gemm_big_kernel<D, GATEUP>), dim3(grid), dim3(512),
-                     kLds, st, (const S*)A, (const S*)B0, (const S*)B1, (S*)C,
-                     offsets, N, K, NB, E, ncol, nseg, nullptr, sw, Gather{},
-                     split);
-  return hipGetLastError();
 }
 
 template <int D>

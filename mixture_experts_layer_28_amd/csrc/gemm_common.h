@@ -181,12 +181,22 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 // The gate+up epilogue's activation (Swiglu in launch.h).  The clamps keep
 // a NaN a NaN (a comparison with NaN is false).
-__device__ __forceinline__ float swiglu_act(float g, float u, Swiglu sw) {
-  if (sw.limit < 0.0f) return silu_mul(g, u);
+__device__ __forceinline__ float swiglu_clipped(float g, float u, Swiglu sw) {
   const float L = sw.limit;
   const float gc = g > L ? L : g;
   const float uc = u < -L ? -L : (u > L ? L : u);
   return gc * sigmoid_fast(sw.alpha * gc) * uc;
+}
+__device__ __forceinline__ float swiglu_act(float g, float u, Swiglu sw) {
+  return sw.limit < 0.0f ? silu_mul(g, u) : swiglu_clipped(g, u, sw);
+}
+// ... chosen at compile time: with the choice at run time the compiler
+// evaluates both forms for every output and selects, which made the
+// plain epilogue carry the clamps and the alpha product.
+template <bool CLIP>
+__device__ __forceinline__ float swiglu_act_t(float g, float u, Swiglu sw) {
+  if constexpr (CLIP) return swiglu_clipped(g, u, sw);
+  else return silu_mul(g, u);
 }
 
 
