@@ -33,10 +33,11 @@
 //   fragments read before it, while the next stage's first fragments are
 //   read (a second register set for up to 4 row tiles, in-place reloads for
 //   5), and the last stage is peeled so no branch merges those waits.
-// * Measured on MI355X: the matrix pipes are busy 50-67 % of the active
-//   cycles and the clock falls to 1.6-1.85 GHz under this load; the rest
+// * Measured on MI355X: the matrix pipes are busy 62-70 % of the active
+//   cycles and the clock falls to 1.58-1.78 GHz under this load; the rest
 //   is operand delivery into the CUs (global -> LDS) and the per-stage
-//   barrier, not the MFMA or LDS-read rates.
+//   barrier, not the MFMA or LDS-read rates (the LDS serves the fragment
+//   reads about a quarter of the time).
 
 #include "gemm_common.h"
 
