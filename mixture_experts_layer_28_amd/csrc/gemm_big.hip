@@ -354,9 +354,14 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   // apart by row / 8 instead left bank conflicts).  Gate+up: a lane's 4
   // gate columns, and the 4 up columns paired with them, are 4 consecutive
   // act columns, so gate (or up) row r = 64a + 4n + j is kept at LDS row
-  // 64a + 16j + n.
+  // 64a + 16j + n.  The weight-gradient form uses the gate+up order for its
+  // plain B rows: its FP32 outputs are 4 bytes wide, and with 4 consecutive
+  // columns per lane in each half of the wave's 128, one 16-byte store of
+  // 16 lanes fills 256 contiguous bytes of a row (8 consecutive columns per
+  // lane left every store instruction filling half of each 128-byte line;
+  // expert backward 1.3 % faster).
   auto bsrc = [](int R) {  // B tile row held at LDS row R
-    return GATEUP ? (R & ~63) | ((R & 15) << 2) | ((R >> 4) & 3)
+    return GATEUP || WG ? (R & ~63) | ((R & 15) << 2) | ((R >> 4) & 3)
                   : (R & ~63) | ((R & 7) << 3) | ((R >> 3) & 7);
   };
 
@@ -436,15 +441,22 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   // outputs of a row and the epilogue stores them as one 16-byte vector.
   // Gate+up: column j < 4 is gate column (lane % 16) * 4 + j of the wave's
   // 64 act columns and j >= 4 the up column of the same act column, so each
-  // lane holds 4 consecutive act outputs of a row.
+  // lane holds 4 consecutive act outputs of a row.  Weight gradients:
+  // column j < 4 is output column (lane % 16) * 4 + j of the wave's 128 and
+  // j >= 4 the same column + 64.
   // (Plain products: B row wn * 128 + (lane % 16) * 8 + j sits at LDS row
   // wn * 128 + 64 * ((lane / 8) % 2) + 8 j + lane % 8; gate+up: gate row
-  // wn * 64 + (lane % 16) * 4 + j at LDS row wn * 64 + 16 j + lane % 16.)
-  const int brow0 = GATEUP ? wn * (TN / 2) + (lane & 15)
-                           : wn * TN + ((lane >> 3) & 1) * 64 + (lane & 7);
+  // wn * 64 + (lane % 16) * 4 + j at LDS row wn * 64 + 16 j + lane % 16;
+  // weight gradients: B row wn * 128 + 64 h + (lane % 16) * 4 + j at LDS
+  // row wn * 128 + 64 h + 16 j + lane % 16, h = 0, 1.)
+  const int brow0 = WG       ? wn * TN + (lane & 15)
+                    : GATEUP ? wn * (TN / 2) + (lane & 15)
+                             : wn * TN + ((lane >> 3) & 1) * 64 + (lane & 7);
   auto bstep = [](int j) -> int {
     constexpr int H2 = FN / 2;
-    return GATEUP ? (j < H2 ? 16 * j : kBN / 2 + 16 * (j - H2)) : 8 * j;
+    return WG       ? (j < H2 ? 16 * j : TN / 2 + 16 * (j - H2))
+           : GATEUP ? (j < H2 ? 16 * j : kBN / 2 + 16 * (j - H2))
+                    : 8 * j;
   };
   const int bswz = swz(brow0);
 
@@ -633,18 +645,19 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       for (int q = 0; q < 4; ++q) {
         const int64_t r = row0 + tr0 + i * 16 + (lane >> 4) * 4 + q;
         if (r >= tend) continue;
-        // NB is a multiple of 8: a lane's group of 8 consecutive columns is
-        // wholly inside or wholly past NB
+        // NB is a multiple of 8: a lane's group of 8 (weight gradients: each
+        // of its two groups of 4) consecutive columns is wholly inside or
+        // wholly past NB
         if constexpr (WG) {
           // M arrives as the kernel's K argument; K is now the expert's rows
           float* cw = Cw + ((int64_t)e * Mw + r) * NB;
-          const int64_t c0 = n0 + wn * TN + (lane & 15) * FN;
-          if (c0 < NB) {
+          const int64_t c0 = n0 + wn * TN + (lane & 15) * 4;
+          if (c0 < NB)
             *(f32x4*)(cw + c0) = f32x4{acc[i][0][q], acc[i][1][q],
                                        acc[i][2][q], acc[i][3][q]};
-            *(f32x4*)(cw + c0 + 4) = f32x4{acc[i][4][q], acc[i][5][q],
-                                           acc[i][6][q], acc[i][7][q]};
-          }
+          if (c0 + TN / 2 < NB)
+            *(f32x4*)(cw + c0 + TN / 2) = f32x4{acc[i][4][q], acc[i][5][q],
+                                                acc[i][6][q], acc[i][7][q]};
           continue;
         }
         S* crow = C + r * NB;
