@@ -142,11 +142,12 @@ __device__ inline void locate_tile(uint32_t b, uint32_t G,
 // ceil(tiles / 8) workgroups on every XCD (the per-wave tile map of the
 // decode kernels, which keeps contiguous XCD ranges).
 inline uint32_t tile_grid(uint32_t tiles) { return 8u * ((tiles + 7u) / 8u); }
-// ... for locate_tile's chunked deal: every XCD holds up to ceil(chunks / 8)
-// chunks of kXcdChunk tiles.
-inline uint32_t tile_grid_chunked(uint32_t tiles) {
-  const uint32_t nch = (tiles + kXcdChunk - 1) / kXcdChunk;
-  return 8u * kXcdChunk * ((nch + 7u) / 8u);
+// ... for a chunked deal (locate_tile's: chunk = kXcdChunk): every XCD
+// holds up to ceil(chunks / 8) chunks of `chunk` tiles.
+inline uint32_t tile_grid_chunked(uint32_t tiles,
+                                  uint32_t chunk = kXcdChunk) {
+  const uint32_t nch = (tiles + chunk - 1) / chunk;
+  return 8u * chunk * ((nch + 7u) / 8u);
 }
 
 __device__ __forceinline__ int swz(int r) { return r & 7; }
