@@ -432,8 +432,7 @@ int moe_combine_backward(const void* y, int dt, int64_t N, int64_t T,
 /*
  * moe_experts_backward_workspace_size - bytes of scratch
  * moe_experts_backward needs (one transposed weight tensor, three [N,I] and
- * two [N,H] intermediates, two [N+8*E,max(H,I)] transposed operand
- * copies).  No passage of the pages: pure host arithmetic of this
+ * two [N,H] intermediates).  No passage of the pages: pure host arithmetic of this
  * library's workspace layout; never touches the device.
  * Returns 0 for invalid arguments.
  */
@@ -457,8 +456,7 @@ size_t moe_experts_backward_workspace_size(int64_t N, int64_t H, int64_t I,
  *               tensor (E*H*I elements of dt), then dact, dgate_raw,
  *               dup_raw [N,I] and the two input-gradient halves
  *               round(dgate_raw . w_gate[e]), round(dup_raw . w_up[e])
- *               [N,H], then two scratch areas of (N+8*E)*max(H,I)
- *               elements, all dt; after the call dact .. the second half
+ *               [N,H], all dt; after the call dact .. the second half
  *               hold the intermediates named below.
  *
  * In the experts page's order, each intermediate rounded to dt:

@@ -20,11 +20,10 @@
 // NT kernels then run at their forward speed.  The weight gradients are
 // "TN" products over each expert's rows,
 //   ddown[e] = dy_e^T . act_e,  dgate[e] = dg_e^T . xd_e,  dup[e] = du_e^T . xd_e;
-// with bf16/f16 each operand's rows are first transposed expert by expert
-// into one contiguous [columns, rows of e] block (seg_transpose_kernel), so
-// the product is an NT GEMM whose K is the expert's row count, run by the
-// prefill GEMM kernel's weight-gradient form (gemm_big.hip); fp32 and
-// unaligned shapes use an LDS-tiled FP32 kernel (tn_kernel).  Elementwise
+// with bf16/f16 the prefill GEMM kernel's weight-gradient form (gemm_big.hip)
+// reads both operands in place, K-major (K is the expert's row count),
+// through the LDS's transposing reads; fp32 and unaligned shapes use an
+// LDS-tiled FP32 kernel (tn_kernel).  Elementwise
 // kernels do the SwiGLU forward and backward and the final add.
 
 #include <initializer_list>
@@ -111,152 +110,6 @@ __global__ __launch_bounds__(256) void transpose16_kernel(
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[t] = tread(tile, w * 8 + t, j);
         *(u32x4*)(dst + c * R + r) = *(const u32x4*)v;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ---- per-expert transpose: block e of out = in[lo:hi, :]^T ------------------
-// in [N, C]; expert e's rows [lo, hi) become the block at out + C*(lo + 8e)
-// laid out [C, Kp] with Kp = hi - lo rounded up to a multiple of 8, the
-// operand form of the weight-gradient GEMM: every row of the block starts
-// 16-byte aligned and its 16-byte chunks never cross into the next row.
-// Columns [hi - lo, Kp) are zeros (seg_pad_kernel).  Rows past offsets[E]
-// are not copied.  Tiles of 64 rows x 64 columns; each tile row's expert is
-// found by a binary search over offsets.
-__host__ __device__ inline int64_t pad8(int64_t n) { return (n + 7) & ~int64_t(7); }
-
-template <typename W>
-__global__ __launch_bounds__(256) void seg_transpose_kernel(
-    const W* __restrict__ in, W* __restrict__ out,
-    const uint32_t* __restrict__ offsets, int E, int64_t N, int64_t C) {
-  __shared__ W tile[64][65];
-  __shared__ int64_t rlo[64], rn[64], rbase[64];
-  int64_t nv = offsets[E];
-  nv = nv < N ? nv : N;
-  const int64_t nr = (nv + 63) / 64, nc = (C + 63) / 64;
-  const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-  for (int64_t b = blockIdx.x; b < nr * nc; b += gridDim.x) {
-    const int64_t rb = b / nc, cb = b % nc;
-    if (threadIdx.x < 64) {
-      const int64_t r = rb * 64 + tx;
-      int lo = 0, hi = E;  // largest e with offsets[e] <= r
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if ((int64_t)offsets[mid] <= r) lo = mid; else hi = mid - 1;
-      }
-      const int64_t a = offsets[lo];
-      int64_t z = lo < E ? (int64_t)offsets[lo + 1] : a;
-      z = z < nv ? z : nv;
-      rlo[tx] = a;
-      rn[tx] = z - a;
-      rbase[tx] = C * (a + 8 * (int64_t)lo);
-    }
-    for (int i = ty; i < 64; i += 4) {
-      const int64_t r = rb * 64 + i, c = cb * 64 + tx;
-      if (r < nv && c < C) tile[i][tx] = in[r * C + c];
-    }
-    __syncthreads();
-    for (int i = ty; i < 64; i += 4) {
-      const int64_t c = cb * 64 + i, r = rb * 64 + tx;
-      if (r < nv && c < C && r >= rlo[tx] && r - rlo[tx] < rn[tx])
-        out[rbase[tx] + c * pad8(rn[tx]) + (r - rlo[tx])] = tile[tx][i];
-    }
-    __syncthreads();
-  }
-}
-
-// Zeros in the padding columns [n, Kp) of every row of every expert's block.
-template <typename W>
-__global__ __launch_bounds__(256) void seg_pad_kernel(
-    W* __restrict__ out, const uint32_t* __restrict__ offsets, int E,
-    int64_t N, int64_t C) {
-  const int64_t total = (int64_t)E * C;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
-       q += (int64_t)gridDim.x * 256) {
-    const int e = (int)(q / C);
-    const int64_t c = q % C;
-    int64_t hi = offsets[e + 1];
-    hi = hi < N ? hi : N;
-    int64_t lo = offsets[e];
-    lo = lo < hi ? lo : hi;
-    const int64_t n = hi - lo, kp = pad8(n);
-    W* row = out + C * (lo + 8 * (int64_t)e) + c * kp;
-    for (int64_t k = n; k < kp; ++k) row[k] = W(0);
-  }
-}
-
-// The same per-expert transpose with 16-byte accesses (16-bit elements, C a
-// multiple of 8, 16-byte aligned).  A workgroup takes a strip of 64 rows of
-// one expert and a range of `ccols` columns; wave 0 finds the strip's
-// expert by a wave prefix sum of ceil(n_e / 64) over the experts.  Rows are
-// loaded as 16-byte column vectors into an LDS tile, and each column is
-// stored as 16-byte vectors of 8 consecutive rows of the expert (k a
-// multiple of 8, so every store is aligned), with zeros past n_e up to Kp:
-// the padding needs no separate pass.
-__global__ __launch_bounds__(256) void seg_transpose16_kernel(
-    const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-    const uint32_t* __restrict__ offsets, int E, int64_t N, int64_t C,
-    int64_t ccols, uint32_t ncg) {
-  __shared__ uint16_t tile[64][64];
-  __shared__ int64_t s_lo, s_n, s_k0, s_base;
-  __shared__ int s_found;
-  const uint32_t strip = blockIdx.x / ncg, cg = blockIdx.x % ncg;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    if (lane == 0) s_found = 0;
-    uint32_t base = 0;
-    for (int s0 = 0; s0 < E; s0 += 64) {
-      const int e = s0 + lane;
-      int64_t lo = 0, n = 0;
-      if (e < E) {
-        int64_t hi = offsets[e + 1];
-        hi = hi < N ? hi : N;
-        lo = offsets[e];
-        lo = lo < hi ? lo : hi;
-        n = hi - lo;
-      }
-      const uint32_t cnt = (uint32_t)((n + 63) / 64);
-      const uint32_t inc = wave_inclusive_sum(cnt, lane);
-      const uint32_t exc = inc - cnt;
-      const bool hit = strip >= base + exc && strip < base + inc;
-      if (__ballot(hit)) {
-        if (hit) {
-          s_lo = lo;
-          s_n = n;
-          s_k0 = (int64_t)(strip - base - exc) * 64;
-          s_base = C * (lo + 8 * (int64_t)e);
-          s_found = 1;
-        }
-        break;
-      }
-      base += __shfl(inc, 63, 64);
-    }
-  }
-  __syncthreads();
-  if (!s_found) return;
-  const int64_t lo = s_lo, n = s_n, k0 = s_k0, obase = s_base;
-  const int64_t kp = pad8(n);
-  const int64_t cend = (cg + 1) * ccols < C ? (cg + 1) * ccols : C;
-  for (int64_t c0 = cg * ccols; c0 < cend; c0 += 64) {
-    for (int q = threadIdx.x; q < 512; q += 256) {
-      const int i = q / 8, v = q % 8;
-      const int64_t k = k0 + i, c = c0 + v * 8;
-      if (k < n && c < C)
-        *(u32x4*)&tile[i][tslot(i, v) * 8] =
-            *(const u32x4*)(in + (lo + k) * C + c);
-    }
-    __syncthreads();
-    for (int q = threadIdx.x; q < 512; q += 256) {
-      const int j = q / 8, w = q % 8;
-      const int64_t c = c0 + j, k = k0 + w * 8;
-      if (c < C && k < kp) {
-        uint16_t v[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          v[t] = k + t < n ? tread(tile, w * 8 + t, j) : 0;
-        *(u32x4*)(out + obase + c * kp + k) = *(const u32x4*)v;
       }
     }
     __syncthreads();
@@ -475,33 +328,6 @@ __global__ __launch_bounds__(256) void tn_kernel(
 }
 
 template <typename W>
-hipError_t seg_transpose(const void* in, void* out, const uint32_t* offsets,
-                         int E, int64_t N, int64_t C, hipStream_t st) {
-  // strips of 64 rows: at most ceil(N / 64) + E of them; columns in ranges
-  // of 512 per workgroup
-  const int64_t ccols = 512;
-  const int64_t ncg = (C + ccols - 1) / ccols;
-  const int64_t strips = (N + 63) / 64 + E;
-  if (sizeof(W) == 2 && C % 8 == 0 && strips * ncg < kMaxGrid * 8 &&
-      ((uintptr_t)in | (uintptr_t)out) % 16 == 0) {
-    hipLaunchKernelGGL(seg_transpose16_kernel, dim3((unsigned)(strips * ncg)),
-                       dim3(256), 0, st, (const uint16_t*)in, (uint16_t*)out,
-                       offsets, E, N, C, ccols, (uint32_t)ncg);
-    return hipGetLastError();
-  }
-  const int64_t blocks = ((N + 63) / 64) * ((C + 63) / 64);
-  hipLaunchKernelGGL((seg_transpose_kernel<W>), dim3(capped(blocks)),
-                     dim3(256), 0, st, (const W*)in, (W*)out, offsets, E, N,
-                     C);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((seg_pad_kernel<W>),
-                     dim3(capped(((int64_t)E * C + 255) / 256)), dim3(256), 0,
-                     st, (W*)out, offsets, E, N, C);
-  return hipGetLastError();
-}
-
-template <typename W>
 hipError_t transpose(const void* in, void* out, int64_t E, int64_t R,
                      int64_t C, hipStream_t st) {
   const int64_t blocks = E * ((R + 63) / 64) * ((C + 63) / 64);
@@ -544,27 +370,17 @@ hipError_t tn_dt(const void* A, int dt, const void* B,
 }
 
 // Weight gradient Cw[e] = A_e^T . B_e over each expert's rows (A [N,M],
-// B [N,NC] in dtype dt): on MFMA through per-expert transposed copies in
-// ta, tb when the shapes allow, else the FMA kernel.
-// tb_ready: tb already holds B's per-expert transpose (a previous call on
-// the same B took the MFMA path); *tb_used reports whether this call did.
+// B [N,NC] in dtype dt): on MFMA, reading both operands K-major in place,
+// when the shapes allow, else the FMA kernel.
 hipError_t wgrad(const void* A, int dt, const void* B,
                  const uint32_t* offsets, int64_t N, int E, int64_t M,
-                 int64_t NC, float* Cw, void* ta, void* tb, hipStream_t st,
-                 bool tb_ready = false, bool* tb_used = nullptr) {
-  const uintptr_t al = (uintptr_t)ta | (uintptr_t)tb | (uintptr_t)Cw;
+                 int64_t NC, float* Cw, hipStream_t st) {
+  const uintptr_t al = (uintptr_t)A | (uintptr_t)B | (uintptr_t)Cw;
   const bool mfma = dt != DT_F32 && M % 8 == 0 && NC % 8 == 0 &&
-                    al % 16 == 0 && 640 * (N + 8) < ((int64_t)1 << 31) &&
-                    M <= INT32_MAX && NC <= INT32_MAX;
-  if (tb_used) *tb_used = mfma;
+                    al % 16 == 0 &&
+                    N * (M > NC ? M : NC) * 2 < ((int64_t)1 << 31);
   if (!mfma) return tn_dt(A, dt, B, offsets, N, E, M, NC, Cw, st);
-  hipError_t err = seg_transpose<uint16_t>(A, ta, offsets, E, N, M, st);
-  if (err == hipSuccess && !tb_ready)
-    err = seg_transpose<uint16_t>(B, tb, offsets, E, N, NC, st);
-  if (err == hipSuccess)
-    err = launch_wgrad_big(ta, dt, N, (int)M, tb, (int)NC, E, offsets, Cw,
-                           st);
-  return err;
+  return launch_wgrad_big(A, dt, N, (int)M, B, (int)NC, E, offsets, Cw, st);
 }
 
 // 16-byte vectors when every pointer is 16-byte aligned and n is a whole
@@ -711,9 +527,6 @@ ExpertsBackwardLayout experts_backward_layout(int64_t N, int64_t H,
   L.du = take((size_t)N * I * s);
   L.dxg = take((size_t)N * H * s);
   L.dxu = take((size_t)N * H * s);
-  // per-expert transposed copies: N rows plus 8 padding rows per expert
-  L.ta = take((size_t)(N + 8 * E) * (H > I ? H : I) * s);
-  L.tb = take((size_t)(N + 8 * E) * (H > I ? H : I) * s);
   L.total = at;
   return L;
 }
@@ -732,14 +545,12 @@ hipError_t launch_experts_backward(
   void* du = ws + L.du;
   void* dxg = ws + L.dxg;
   void* dxu = ws + L.dxu;
-  void* ta = ws + L.ta;
-  void* tb = ws + L.tb;
   // down projection: input gradient through Wd^T [E,I,H], weight gradient
   hipError_t err = transpose_dt(w_down, dt, wt, E, H, I, st);
   if (err == hipSuccess)
     err = launch_grouped_nt(dy, dt, N, H, wt, I, E, offsets, dact, st);
   if (err == hipSuccess)
-    err = wgrad(dy, dt, act, offsets, N, E, H, I, dwd, ta, tb, st);
+    err = wgrad(dy, dt, act, offsets, N, E, H, I, dwd, st);
   // SwiGLU backward
   if (err == hipSuccess)
     err = MOE_BY_DT(dt, elementwise_bwd, gate, up, dact, dg, du, N * I, st);
@@ -753,14 +564,10 @@ hipError_t launch_experts_backward(
     err = launch_grouped_nt(du, dt, N, I, wt, H, E, offsets, dxu, st);
   if (err == hipSuccess)
     err = MOE_BY_DT(dt, elementwise_add, dxg, dxu, dxd, N * H, st);
-  bool xd_in_tb = false;
   if (err == hipSuccess)
-    err = wgrad(dg, dt, xd, offsets, N, E, I, H, dwg, ta, tb, st, false,
-                &xd_in_tb);
-  // xd's per-expert transpose from the gate's weight gradient is still in
-  // tb if that call made one (same stream, same shapes)
+    err = wgrad(dg, dt, xd, offsets, N, E, I, H, dwg, st);
   if (err == hipSuccess)
-    err = wgrad(du, dt, xd, offsets, N, E, I, H, dwu, ta, tb, st, xd_in_tb);
+    err = wgrad(du, dt, xd, offsets, N, E, I, H, dwu, st);
   return err;
 }
 

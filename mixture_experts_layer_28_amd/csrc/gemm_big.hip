@@ -60,9 +60,15 @@ constexpr int kBM = 320, kBN = 256, kBK = 64;
 constexpr int kSplitUnits = 9;
 // Weight-gradient tiles per XCD chunk (see the weight-gradient form below).
 constexpr uint32_t kWgChunk = 4;
+// Weight-gradient tiles: kWgBM x kBN outputs; K-major stage parts of 16
+// groups of 4 K rows, each group 4 x 256 elements + 32 of padding.
+constexpr int kWgBM = 256;
+constexpr int kWgGroup = 4 * 256 + 32;
+constexpr int kWgPart = 16 * kWgGroup;
 constexpr int kFM = kBM / 4 / 16;                 // MFMA row tiles per wave, at most
 constexpr int kStage = (kBM + kBN) * kBK;         // elements of one LDS stage
 constexpr size_t kLds = 2 * kStage * 2;           // two stages of 16-bit data
+static_assert(2 * kWgPart <= kStage, "both K-major parts fit a stage");
 
 // Opt a kernel in to kLds bytes of dynamic LDS, once per device (the
 // attribute belongs to each device's copy of the kernel); `done` holds one
@@ -224,20 +230,19 @@ __device__ __forceinline__ void tiny_tile(
 }
 
 // WG: the weight-gradient form.  Per expert e with rows [lo, hi) of a
-// dispatch, Cw[e] [M, NB] (FP32) = A_e . B_e^T with A_e = A + (lo + 8e) * M
-// holding [M, Kp] and B_e = B0 + (lo + 8e) * NB holding [NB, Kp], Kp =
-// hi - lo rounded up to a multiple of 8 with zeros past hi - lo (each
-// expert's rows transposed into one block whose rows are 16-byte aligned),
-// so K = Kp varies per expert.  The tiles are E x ceil(M / kBM) x ncol
-// (row blocks of equal size), dealt to the XCDs in chunks of kWgChunk
-// tiles, round robin.  A tile's cost grows with its expert's rows:
-// contiguous ranges of equal tile counts per XCD gave the XCD holding the
-// largest experts of a skewed routing about 1.5 times the mean work (the
-// fine-grained expert backward ran 19 % faster with chunks of 4; chunks of
-// 2, 8, 16, 32 and 64 measured 17.3, 17.3, 17.8, 17.8 and 18.6 ms against
-// 17.2, and the balanced Mixtral-shaped backward stayed within 1 %).  An
-// expert without rows writes zeros.  N is the row count of the dispatch, M passes
-// in `K`.
+// dispatch, Cw[e] [M, NB] (FP32) = A_e^T . B_e with A_e = rows lo .. hi-1 of
+// A [N, M] and B_e = the same rows of B0 [N, NB]: both operands are read in
+// place, K-major (K = hi - lo, the expert's row count), into LDS groups of
+// 4 K rows and out of LDS with transposing reads (no per-expert transposed
+// copies).  The tiles are E x ceil(M / kWgBM) x ncol (row blocks of whole
+// 16-row units), dealt to the XCDs in chunks of kWgChunk tiles, round
+// robin.  A tile's cost grows with its expert's rows: contiguous ranges of
+// equal tile counts per XCD gave the XCD holding the largest experts of a
+// skewed routing about 1.5 times the mean work (the fine-grained expert
+// backward ran 19 % faster with chunks of 4; chunks of 2, 8, 16, 32 and 64
+// measured 17.3, 17.3, 17.8, 17.8 and 18.6 ms against 17.2, and the
+// balanced Mixtral-shaped backward stayed within 1 %).  An expert without
+// rows writes zeros.  N is the row count of the dispatch, M passes in `K`.
 // GATHER (gate+up only): A row r of the segments is row ga.rows[r] of the
 // token rows x = A [ga.xrows, K] instead of row r of the dispatched copy.
 // CLIP: the clipped SwiGLU activation (gate+up only).
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   constexpr int TCOLS = GATEUP ? kBN / 2 : kBN;
   constexpr int NBLK = (kBM + kBN) / 8;           // 1 KB LDS blocks per stage
   constexpr int ABLK = kBM / 8;
-  constexpr int BLK = NBLK / 8;                   // ... per wave
+  constexpr int BLK = WG ? 8 : NBLK / 8;          // ... per wave
   static_assert(NBLK % 8 == 0, "blocks per wave");
   static_assert(!GATEUP || FN % 2 == 0, "gate/up halves");
   static_assert(FN == 8, "an 8-column group per lane: one 16-byte vector");
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   if constexpr (WG) {
     // static map: tile L -> (expert, row block, column block)
     const int64_t M = K;
-    const uint32_t nmb = (uint32_t)((M + kBM - 1) / kBM);
+    const uint32_t nmb = (uint32_t)((M + kWgBM - 1) / kWgBM);
     const uint32_t total = (uint32_t)E * nmb * ncol;
     const uint32_t local = blockIdx.x / 8u, q = local / kWgChunk;
     const uint32_t L =
@@ -291,16 +296,20 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const uint32_t rem = l - grp * 8u * ncol;
     const int64_t mb = first + rem % gs;
     n0 = (int64_t)(rem / gs) * TCOLS;
-    const int64_t a = mb * M / nmb, z = (mb + 1) * M / nmb;
+    // row blocks of whole 16-row units: every block starts 32-byte aligned
+    // in a K-major row, so no 16-byte operand chunk straddles a buffer end
+    const int64_t u16 = (M + 15) / 16;
+    const int64_t a = 16 * (mb * u16 / nmb);
+    const int64_t z0 = 16 * ((mb + 1) * u16 / nmb), z = z0 < M ? z0 : M;
     row0 = a;
     arows = (int)(z - a);
     int64_t hi = uniform((int64_t)offsets[e + 1]);
     hi = hi < N ? hi : N;
     int64_t lo = uniform((int64_t)offsets[e]);
     lo = lo < hi ? lo : hi;
-    K = (int)(((hi - lo) + 7) & ~int64_t(7));
-    Ab = A + (lo + 8 * (int64_t)e) * M;
-    Bb = B0 + (lo + 8 * (int64_t)e) * (int64_t)NB;
+    K = (int)(hi - lo);
+    Ab = A + lo * M;
+    Bb = B0 + lo * (int64_t)NB;
     if (K == 0) {  // no rows: a zero gradient
       float* ce = Cw + (int64_t)e * M * NB;
       for (int q = tid; q < kBM * TCOLS; q += NT) {
@@ -342,11 +351,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   // and OOB (2^31) is always past the end; in the weight-gradient form B's
   // resource spans the tile's columns only, too
   const __amdgpu_buffer_rsrc_t rA =
-      GATHER ? make_rsrc(A, (uint64_t)ga.xrows * rowbytes)
-             : make_rsrc(Ab + row0 * K, (uint64_t)arows * rowbytes);
+      WG       ? make_rsrc(Ab, (uint64_t)K * (uint64_t)Mw * sizeof(S))
+      : GATHER ? make_rsrc(A, (uint64_t)ga.xrows * rowbytes)
+               : make_rsrc(Ab + row0 * K, (uint64_t)arows * rowbytes);
   const int64_t bcols = NB - n0 < kBN ? NB - n0 : kBN;
   const __amdgpu_buffer_rsrc_t rB0 =
-      WG ? make_rsrc(Bb + n0 * K, (uint64_t)bcols * rowbytes)
+      WG ? make_rsrc(Bb, (uint64_t)K * (uint64_t)NB * sizeof(S))
          : make_rsrc(B0 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes);
   const __amdgpu_buffer_rsrc_t rB1 =
       GATEUP ? make_rsrc(B1 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes)
@@ -363,14 +373,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   // apart by row / 8 instead left bank conflicts).  Gate+up: a lane's 4
   // gate columns, and the 4 up columns paired with them, are 4 consecutive
   // act columns, so gate (or up) row r = 64a + 4n + j is kept at LDS row
-  // 64a + 16j + n.  The weight-gradient form uses the gate+up order for its
-  // plain B rows: its FP32 outputs are 4 bytes wide, and with 4 consecutive
-  // columns per lane in each half of the wave's 128, one 16-byte store of
-  // 16 lanes fills 256 contiguous bytes of a row (8 consecutive columns per
-  // lane left every store instruction filling half of each 128-byte line;
-  // expert backward 1.3 % faster).
+  // 64a + 16j + n.
   auto bsrc = [](int R) {  // B tile row held at LDS row R
-    return GATEUP || WG ? (R & ~63) | ((R & 15) << 2) | ((R >> 4) & 3)
+    return GATEUP ? (R & ~63) | ((R & 15) << 2) | ((R >> 4) & 3)
                   : (R & ~63) | ((R & 7) << 3) | ((R >> 3) & 7);
   };
 
@@ -398,6 +403,41 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   }
   auto dma = [&](int k0, int st) {
     S* base = sm + st * kStage;
+    if constexpr (WG) {
+      // K-major operands, 4 K rows at a time: the A part (then the B part)
+      // of a stage holds, per group q of 4 K rows, 16 slots of 16 columns
+      // (64 bytes each row, the 4 rows one after another) and 64 bytes of
+      // padding: 16-byte chunk w of a group is slot w / 8, row (w / 2) % 4,
+      // columns 8 (w % 2) .. + 7 of the slot.  The padding puts groups 2
+      // apart (the ones a transposing read takes for lanes 0-15 and 16-31)
+      // on different halves of the 256-byte bank cycle.  Each wave loads
+      // 4 A and 4 B blocks of 1 KB (half a group); chunks past K or past
+      // the matrix read zeros.
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int b = wid + 8 * (j & 3), q = b >> 1, w = 64 * (b & 1) + lane;
+        const int k = k0 + 4 * q + ((w >> 1) & 3);
+        const int c = 16 * (w >> 3) + 8 * (w & 1);
+        S* dst = base + (j < 4 ? 0 : kWgPart) + q * kWgGroup + 512 * (b & 1);
+        if (j < 4) {
+          const int m = (int)row0 + c;
+          const uint32_t o =
+              k < K && m < Mw
+                  ? ((uint32_t)k * (uint32_t)Mw + (uint32_t)m) * sizeof(S)
+                  : OOB;
+          buffer_load_lds16(rA, dst, o);
+        } else {
+          const int n = (int)n0 + c;
+          uint32_t o =
+              k < K && n < NB
+                  ? ((uint32_t)k * (uint32_t)NB + (uint32_t)n) * sizeof(S)
+                  : OOB;
+          asm volatile("" : "+v"(o));
+          buffer_load_lds16(rB0, dst, o);
+        }
+      }
+      return;
+    }
     // branch-free: which slots hold A or B blocks, and which B rows are
     // up rows, is fixed per unrolled slot (wid < 8), so the issue is
     // straight-line code (it was a chain of uniform branches per block)
@@ -450,26 +490,47 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   // outputs of a row and the epilogue stores them as one 16-byte vector.
   // Gate+up: column j < 4 is gate column (lane % 16) * 4 + j of the wave's
   // 64 act columns and j >= 4 the up column of the same act column, so each
-  // lane holds 4 consecutive act outputs of a row.  Weight gradients:
-  // column j < 4 is output column (lane % 16) * 4 + j of the wave's 128 and
-  // j >= 4 the same column + 64.
+  // lane holds 4 consecutive act outputs of a row.
   // (Plain products: B row wn * 128 + (lane % 16) * 8 + j sits at LDS row
   // wn * 128 + 64 * ((lane / 8) % 2) + 8 j + lane % 8; gate+up: gate row
-  // wn * 64 + (lane % 16) * 4 + j at LDS row wn * 64 + 16 j + lane % 16;
-  // weight gradients: B row wn * 128 + 64 h + (lane % 16) * 4 + j at LDS
-  // row wn * 128 + 64 h + 16 j + lane % 16, h = 0, 1.)
-  const int brow0 = WG       ? wn * TN + (lane & 15)
-                    : GATEUP ? wn * (TN / 2) + (lane & 15)
-                             : wn * TN + ((lane >> 3) & 1) * 64 + (lane & 7);
+  // wn * 64 + (lane % 16) * 4 + j at LDS row wn * 64 + 16 j + lane % 16.)
+  const int brow0 = GATEUP ? wn * (TN / 2) + (lane & 15)
+                           : wn * TN + ((lane >> 3) & 1) * 64 + (lane & 7);
   auto bstep = [](int j) -> int {
     constexpr int H2 = FN / 2;
-    return WG       ? (j < H2 ? 16 * j : TN / 2 + 16 * (j - H2))
-           : GATEUP ? (j < H2 ? 16 * j : kBN / 2 + 16 * (j - H2))
-                    : 8 * j;
+    return GATEUP ? (j < H2 ? 16 * j : kBN / 2 + 16 * (j - H2)) : 8 * j;
   };
   const int bswz = swz(brow0);
 
   const int nk = (K + kBK - 1) / kBK;
+  // Weight gradients: the fragment of columns c0 .. c0+15 (c0 a multiple
+  // of 16) of a K-major stage part, at K rows 32 half +
+  // 8 (lane / 16) + 0..7, from two transposing 8-byte LDS reads.  In each
+  // 16-lane group, source lane s addresses K row 4 rd + s / 4 of the
+  // group's 8 and columns c0 + 4 (s % 4) .. + 3, so the 16 lanes read 128
+  // contiguous bytes (one slot of four rows: no bank conflict); lane
+  // 4 r + p receives column c0 + 4 r + p of those four rows.
+  auto tr_frag = [&](const S* T, int half, int c0) -> V {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    s4 t[2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int kq = 8 * half + 2 * (lane >> 4) + rd;  // group of 4 K rows
+      const S* p = T + kq * kWgGroup + (c0 >> 4) * 64 + 4 * (lane & 15);
+      t[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p);
+    }
+    V v;
+    __builtin_memcpy(&v, t, sizeof(v));
+    return v;
+  };
+  // Weight gradients multiply with the operands swapped (B fragment as the
+  // MFMA's first operand): the accumulators then hold the transposed tile,
+  // so lane l has Cw row (l % 16) and 4 consecutive columns 4 (l / 16) + q.
+  auto mm = [](V a, V b, f32x4 c) -> f32x4 {
+    if constexpr (WG) return Frag<D>::mma(b, a, c);
+    else return Frag<D>::mma(a, b, c);
+  };
   // The K loop and epilogue of a wave with FMC MFMA row tiles (0: it only
   // loads).  Each count has its own accumulators, so a wave with fewer row
   // tiles holds no idle accumulator registers.
@@ -484,6 +545,15 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     auto read_frags = [&](int st, int half, V* fa, V* fb) {
       const S* As = sm + st * kStage;
       const S* Bs = As + kBM * kBK;
+      if constexpr (WG) {
+#pragma unroll
+        for (int i = 0; i < FMC; ++i)
+          fa[i] = tr_frag(As, half, tr0 + 16 * i);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[j] = tr_frag(As + kWgPart, half, wn * TN + 16 * j);
+        return;
+      }
       const int c = half * 4 + (lane >> 4);
 #pragma unroll
       for (int i = 0; i < FMC; ++i) {
@@ -499,8 +569,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 #pragma unroll
       for (int i = 0; i < FMC; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mm(fa[i], fb[j], acc[i][j]);
     };
     dma(0, 0);
     if (nk > 1) {
@@ -508,8 +577,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       // latency overlaps stage 0's; a raw barrier, because __syncthreads'
       // release fence would wait for stage 1 as well
       dma(kBK, 1);
-      static_assert(BLK == 9, "the count below leaves one stage in flight");
-      asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
+      // the count leaves one stage's loads in flight
+      if constexpr (BLK == 9)
+        asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
+      else {
+        static_assert(BLK == 8, "one stage's loads per wave");
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      }
     } else {
       wait_vmem();
       __syncthreads();
@@ -576,12 +650,16 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       // The barrier sits between the halves and the last K step is peeled,
       // as above.
       auto read_a = [&](int st, int half, int i) -> V {
+        if constexpr (WG)
+          return tr_frag(sm + st * kStage, half, tr0 + 16 * i);
         const S* As = sm + st * kStage;
         const int c = half * 4 + (lane >> 4);
         const int r = tr0 + i * 16 + (lane & 15);
         return *(const V*)&As[r * kBK + ((c ^ swz(r)) << 3)];
       };
       auto read_b = [&](int st, int half, int j) -> V {
+        if constexpr (WG)
+          return tr_frag(sm + st * kStage + kWgPart, half, wn * TN + 16 * j);
         const S* Bs = sm + st * kStage + kBM * kBK;
         const int c = half * 4 + (lane >> 4);
         return *(const V*)&Bs[(brow0 + bstep(j)) * kBK + ((c ^ bswz) << 3)];
@@ -592,7 +670,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         for (int j = 0; j < FN - 2; ++j) {
 #pragma unroll
           for (int i = 0; i < FMC; ++i)
-            acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
+            acc[i][j] = mm(fa[i], fb[j], acc[i][j]);
           if (reload) fb[j] = read_b(st2, half2, j);
         }
         // the last two columns row by row, so each A fragment is reloaded
@@ -601,7 +679,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         for (int i = 0; i < FMC; ++i) {
 #pragma unroll
           for (int j = FN - 2; j < FN; ++j)
-            acc[i][j] = Frag<D>::mma(fa[i], fb[j], acc[i][j]);
+            acc[i][j] = mm(fa[i], fb[j], acc[i][j]);
           if (reload) fa[i] = read_a(st2, half2, i);
         }
         if (reload) {
@@ -648,6 +726,21 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       }
     }
 
+    if constexpr (WG) {
+      // M arrives as the kernel's K argument; K is now the expert's rows
+#pragma unroll
+      for (int i = 0; i < FMC; ++i) {
+        const int64_t r = row0 + tr0 + i * 16 + (lane & 15);
+        if (r >= tend) continue;
+        float* cw = Cw + ((int64_t)e * Mw + r) * NB;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t c = n0 + wn * TN + 16 * j + 4 * (lane >> 4);
+          if (c < NB) *(f32x4*)(cw + c) = acc[i][j];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < FMC; ++i) {
 #pragma unroll
@@ -657,18 +750,6 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         // NB is a multiple of 8: a lane's group of 8 (weight gradients: each
         // of its two groups of 4) consecutive columns is wholly inside or
         // wholly past NB
-        if constexpr (WG) {
-          // M arrives as the kernel's K argument; K is now the expert's rows
-          float* cw = Cw + ((int64_t)e * Mw + r) * NB;
-          const int64_t c0 = n0 + wn * TN + (lane & 15) * 4;
-          if (c0 < NB)
-            *(f32x4*)(cw + c0) = f32x4{acc[i][0][q], acc[i][1][q],
-                                       acc[i][2][q], acc[i][3][q]};
-          if (c0 + TN / 2 < NB)
-            *(f32x4*)(cw + c0 + TN / 2) = f32x4{acc[i][4][q], acc[i][5][q],
-                                                acc[i][6][q], acc[i][7][q]};
-          continue;
-        }
         S* crow = C + r * NB;
         if (GATEUP) {
           // act columns 4 (lane % 16) .. + 3 of the wave's 64: one 8-byte
@@ -766,7 +847,7 @@ hipError_t launch_wgrad_big(const void* A, int dt, int64_t N, int M,
                             const uint32_t* offsets, float* Cw,
                             hipStream_t st) {
   const uint32_t ncol = cdiv(NC, kBN);
-  const uint32_t nmb = cdiv(M, kBM);
+  const uint32_t nmb = cdiv(M, kWgBM);
   const uint32_t grid = tile_grid_chunked((uint32_t)E * nmb * ncol, kWgChunk);
   if (dt == DT_BF16) {
     using S = typename Storage<DT_BF16>::T;

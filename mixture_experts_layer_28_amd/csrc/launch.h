@@ -161,7 +161,7 @@ hipError_t launch_combine_backward(const void* y, int dt, int64_t N,
 // [N,I], the two input-gradient halves [N,H], and two per-expert transposed
 // operand copies of N * max(H, I) elements (byte offsets, 256-aligned).
 struct ExpertsBackwardLayout {
-  size_t wt, dact, dg, du, dxg, dxu, ta, tb, total;
+  size_t wt, dact, dg, du, dxg, dxu, total;
 };
 ExpertsBackwardLayout experts_backward_layout(int64_t N, int64_t H,
                                               int64_t I, int64_t E, int dt);

@@ -316,10 +316,10 @@ def test_experts_backward_workspace_and_rejects():
     L = _lib.lib()
     N, H, I, E = 100, 64, 32, 4
     ws = L.moe_experts_backward_workspace_size(N, H, I, E, 2)
-    # one transposed weight tensor, three [N,I], two [N,H] and two
-    # [N+8E,max(H,I)] buffers
-    assert ws >= (E * H * I + 3 * N * I + 2 * N * H
-                  + 2 * (N + 8 * E) * H) * 2 and ws % 256 == 0
+    # one transposed weight tensor, three [N,I] and two [N,H] buffers, each
+    # starting 256-byte aligned
+    parts = (E * H * I + 3 * N * I + 2 * N * H) * 2
+    assert parts <= ws <= parts + 6 * 256 and ws % 256 == 0
     assert L.moe_experts_backward_workspace_size(N, H, I, 0, 2) == 0
     assert L.moe_experts_backward_workspace_size(N, H, I, E, 7) == 0
     args = [FAKE, 2, N, H, I, E, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,

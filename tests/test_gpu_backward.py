@@ -157,7 +157,10 @@ def test_tiny_fp32():
 
 @pytest.mark.parametrize("T,H,I,E,k", [
     (45, 136, 200, 5, 2), (260, 64, 96, 12, 3), (1, 32, 16, 4, 4),
-    (300, 128, 256, 8, 2), (129, 128, 64, 16, 8)])
+    (300, 128, 256, 8, 2), (129, 128, 64, 16, 8),
+    # weight gradients of several row blocks (M = 712 and 968: blocks of
+    # 16-row units, the last unit half full) and ragged column blocks
+    (96, 968, 712, 4, 2)])
 def test_ragged_bf16(T, H, I, E, k):
     wl = workloads.make("edge", T=T, H=H, I=I, E=E, k=k)
     wl["logits"] = torch.nan_to_num(wl["logits"].float(), nan=0.0,
