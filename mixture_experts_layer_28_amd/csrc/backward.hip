@@ -11,13 +11,14 @@
 // input gradients.  Every tensor that order materialises is rounded to the
 // storage dtype; weight gradients are FP32.
 //
-// The products reuse the grouped NT GEMMs of the forward:
-//   gate = xd . Wg^T, up = xd . Wu^T            (training forward)
-//   dact = dy . Wd        = NT(dy, Wd^T)        (Wd^T [E,I,H], transposed)
-//   dxg  = dg . Wg        = NT(dg, Wg^T)        (Wg^T [E,H,I], transposed)
-//   dxu  = du . Wu        = NT(du, Wu^T)
-// The transposes cost one read and one write of a weight tensor each; the
-// NT kernels then run at their forward speed.  The weight gradients are
+// The products run on the forward's grouped GEMMs:
+//   gate = xd . Wg^T, up = xd . Wu^T            (training forward, NT)
+//   dact = dy . Wd,  dxg = dg . Wg,  dxu = du . Wu
+// The input gradients take the prefill kernel's NN form, which reads the
+// weights K-major in place through the LDS's transposing reads; shapes it
+// does not take (fp32, unaligned, decode-sized segments) go through a
+// transposed weight copy (one read and one write of the weight tensor) and
+// the NT kernels.  The weight gradients are
 // "TN" products over each expert's rows,
 //   ddown[e] = dy_e^T . act_e,  dgate[e] = dg_e^T . xd_e,  dup[e] = du_e^T . xd_e;
 // with bf16/f16 the prefill GEMM kernel's weight-gradient form (gemm_big.hip)
@@ -531,6 +532,24 @@ ExpertsBackwardLayout experts_backward_layout(int64_t N, int64_t H,
   return L;
 }
 
+// C = A . W_e per segment, W [E, K, NB]: on the prefill kernel's NN form
+// (W read K-major in place) when the shapes allow, else through a
+// transposed copy of W in wt and the NT products.
+hipError_t grouped_nn(const void* A, int dt, int64_t N, int64_t K,
+                      const void* W, int64_t NB, int E,
+                      const uint32_t* offsets, void* C, void* wt,
+                      hipStream_t st) {
+  const uintptr_t al = (uintptr_t)A | (uintptr_t)W | (uintptr_t)C;
+  const int64_t lim = (int64_t)1 << 31;
+  if (dt != DT_F32 && K % 8 == 0 && NB % 8 == 0 && al % 16 == 0 &&
+      N >= 96 * (int64_t)E && K * NB * 2 < lim && 320 * K * 2 < lim)
+    return launch_nn_big(A, dt, N, (int)K, W, (int)NB, E, offsets, C, st);
+  hipError_t err = transpose_dt(W, dt, wt, E, K, NB, st);
+  if (err == hipSuccess)
+    err = launch_grouped_nt(A, dt, N, K, wt, NB, E, offsets, C, st);
+  return err;
+}
+
 hipError_t launch_experts_backward(
     const void* xd, int dt, int64_t N, int64_t H, int64_t I, int E,
     const void* w_gate, const void* w_up, const void* w_down,
@@ -545,10 +564,10 @@ hipError_t launch_experts_backward(
   void* du = ws + L.du;
   void* dxg = ws + L.dxg;
   void* dxu = ws + L.dxu;
-  // down projection: input gradient through Wd^T [E,I,H], weight gradient
-  hipError_t err = transpose_dt(w_down, dt, wt, E, H, I, st);
-  if (err == hipSuccess)
-    err = launch_grouped_nt(dy, dt, N, H, wt, I, E, offsets, dact, st);
+  // down projection: input gradient through Wd [E,H,I] read K-major (or a
+  // transposed copy), weight gradient
+  hipError_t err = grouped_nn(dy, dt, N, H, w_down, I, E, offsets, dact, wt,
+                              st);
   if (err == hipSuccess)
     err = wgrad(dy, dt, act, offsets, N, E, H, I, dwd, st);
   // SwiGLU backward
@@ -556,12 +575,10 @@ hipError_t launch_experts_backward(
     err = MOE_BY_DT(dt, elementwise_bwd, gate, up, dact, dg, du, N * I, st);
   // gate and up projections: input gradients through Wg^T, Wu^T [E,H,I]
   // (one transposed copy at a time), weight gradients, then the sum
-  if (err == hipSuccess) err = transpose_dt(w_gate, dt, wt, E, I, H, st);
   if (err == hipSuccess)
-    err = launch_grouped_nt(dg, dt, N, I, wt, H, E, offsets, dxg, st);
-  if (err == hipSuccess) err = transpose_dt(w_up, dt, wt, E, I, H, st);
+    err = grouped_nn(dg, dt, N, I, w_gate, H, E, offsets, dxg, wt, st);
   if (err == hipSuccess)
-    err = launch_grouped_nt(du, dt, N, I, wt, H, E, offsets, dxu, st);
+    err = grouped_nn(du, dt, N, I, w_up, H, E, offsets, dxu, wt, st);
   if (err == hipSuccess)
     err = MOE_BY_DT(dt, elementwise_add, dxg, dxu, dxd, N * H, st);
   if (err == hipSuccess)

@@ -245,9 +245,11 @@ __device__ __forceinline__ void tiny_tile(
 // rows writes zeros.  N is the row count of the dispatch, M passes in `K`.
 // GATHER (gate+up only): A row r of the segments is row ga.rows[r] of the
 // token rows x = A [ga.xrows, K] instead of row r of the dispatched copy.
-// CLIP: the clipped SwiGLU activation (gate+up only).
+// ALT: with GATEUP, the clipped SwiGLU activation; on a plain product, the
+// NN form: B is stored K-major ([E, K, NB], e.g. a weight tensor used
+// untransposed) and read through the LDS's transposing reads.
 template <int D, bool GATEUP, bool WG = false, bool GATHER = false,
-          bool CLIP = false>
+          bool ALT = false>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const typename Storage<D>::T* __restrict__ A,
     const typename Storage<D>::T* __restrict__ B0,
@@ -258,6 +260,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     Swiglu sw = Swiglu{}, Gather ga = Gather{}, int split = 0) {
   using S = typename Storage<D>::T;
   using V = typename Frag<D>::V;
+  constexpr bool CLIP = GATEUP && ALT;
+  constexpr bool NN = !GATEUP && !WG && ALT;
   constexpr int WN = 2, NT = 512;
   constexpr int TN = kBN / WN;                    // 128 columns per wave
   constexpr int FN = TN / 16;                     // 8 MFMA column tiles
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     }
     return;
   }
-  if (!WG && arows <= kTinyRows) {
+  if (!WG && !NN && arows <= kTinyRows) {
     tiny_tile<D, GATEUP, GATHER, CLIP>(A, B0, B1, C, ga.rows, ga.xrows, row0,
                                  arows, n0, e, K, NB, sw);
     return;
@@ -465,6 +469,23 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         const uint32_t ro = GATHER ? ao[j] : (uint32_t)r * rowbytes;
         buffer_load_lds16(rA, base + b * 512,
                           kk < K ? ro + kk * (uint32_t)sizeof(S) : OOB);
+      } else if constexpr (NN) {
+        // K-major B: group q of 4 K rows holds 16 slots of 16 columns (the
+        // 4 rows' 16 columns one after another, 128 bytes); slot t holds
+        // columns 16 (t ^ ((q / 2) % 2)) .. + 15, which puts the two groups
+        // a transposing read takes for lanes 0-15 and 16-31 on different
+        // halves of the 256-byte bank cycle
+        const int bb = wid + 8 * (j - AJ);  // B block: half a group
+        const int q = bb >> 1, w = 64 * (bb & 1) + lane;
+        const int n =
+            (int)n0 + 16 * ((w >> 3) ^ ((q >> 1) & 1)) + 8 * (w & 1);
+        const int k = k0 + 4 * q + ((w >> 1) & 3);
+        uint32_t bo =
+            k < K && n < NB
+                ? ((uint32_t)k * (uint32_t)NB + (uint32_t)n) * sizeof(S)
+                : OOB;
+        asm volatile("" : "+v"(bo));
+        buffer_load_lds16(rB0, base + (ABLK + bb) * 512, bo);
       } else {
         const int bb = wid + 8 * (j - AJ);  // B block
         const int R = 8 * bb + (lane >> 3);
@@ -524,6 +545,27 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     __builtin_memcpy(&v, t, sizeof(v));
     return v;
   };
+  // NN: the B fragment of columns c0 .. c0+15 (c0 = 128 wn + 16 j) at K
+  // rows 32 half + 8 (lane / 16) + 0..7, from two transposing reads of the
+  // K-major B part (slots rotated by (q / 2) % 2 = (lane / 16) % 2; the
+  // rotation flips bit 0 of the slot, j's parity, so the address stays a
+  // per-lane base plus a constant)
+  auto tr_frag_nn = [&](const S* T, int half, int c0) -> V {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    const int xo = ((lane >> 4) & 1) * 64;
+    s4 t[2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int kq = 8 * half + 2 * (lane >> 4) + rd;
+      const S* p = T + kq * 4 * kBN + (c0 >> 4) * 64 +
+                   (((c0 >> 4) & 1) ? -xo : xo) + 4 * (lane & 15);
+      t[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p);
+    }
+    V v;
+    __builtin_memcpy(&v, t, sizeof(v));
+    return v;
+  };
   // Weight gradients multiply with the operands swapped (B fragment as the
   // MFMA's first operand): the accumulators then hold the transposed tile,
   // so lane l has Cw row (l % 16) and 4 consecutive columns 4 (l / 16) + q.
@@ -562,7 +604,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        fb[j] = *(const V*)&Bs[(brow0 + bstep(j)) * kBK + ((c ^ bswz) << 3)];
+        if constexpr (NN)
+          fb[j] = tr_frag_nn(Bs, half, wn * TN + 16 * j);
+        else
+          fb[j] = *(const V*)&Bs[(brow0 + bstep(j)) * kBK + ((c ^ bswz) << 3)];
       }
     };
     auto mma = [&](const V* fa, const V* fb) {
@@ -660,6 +705,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       auto read_b = [&](int st, int half, int j) -> V {
         if constexpr (WG)
           return tr_frag(sm + st * kStage + kWgPart, half, wn * TN + 16 * j);
+        if constexpr (NN)
+          return tr_frag_nn(sm + st * kStage + kBM * kBK, half, wn * TN + 16 * j);
         const S* Bs = sm + st * kStage + kBM * kBK;
         const int c = half * 4 + (lane >> 4);
         return *(const V*)&Bs[(brow0 + bstep(j)) * kBK + ((c ^ bswz) << 3)];
@@ -768,6 +815,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
             u32x2 pk;
             __builtin_memcpy(&pk, v, sizeof(pk));
             *(u32x2*)(crow + c0) = pk;
+          }
+        } else if constexpr (NN) {
+          // column j of a lane is output column 16 j + lane % 16
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t c = n0 + wn * TN + 16 * j + (lane & 15);
+            if (c < NB) crow[c] = from_f32<D>(acc[i][j][q]);
           }
         } else {
           const int64_t c0 = n0 + wn * TN + (lane & 15) * FN;
@@ -882,6 +936,31 @@ hipError_t launch_nt_big(const void* A, int dt, int64_t N, int K,
                                       st);
   return launch_one<DT_F16, false>(A, B, B, C, offsets, N, K, NB, E, E + 1,
                                    st);
+}
+
+// C = A . B_e per segment with B stored K-major ([E, K, NB]): the NN form.
+hipError_t launch_nn_big(const void* A, int dt, int64_t N, int K,
+                         const void* B, int NB, int E,
+                         const uint32_t* offsets, void* C, hipStream_t st) {
+  const uint32_t ncol = cdiv(NB, kBN);
+  const int nseg = E + 1;  // rows past offsets[E] are written as zeros
+  const uint32_t grid =
+      tile_grid_chunked(ncol * (cdiv(N, 256) + (uint32_t)nseg));
+  auto go = [&](auto d_c) -> hipError_t {
+    constexpr int DD = decltype(d_c)::value;
+    using S = typename Storage<DD>::T;
+    static std::atomic<uint64_t> attr{0};
+    hipError_t err = allow_lds(
+        (const void*)gemm_big_kernel<DD, false, false, false, true>, attr);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((gemm_big_kernel<DD, false, false, false, true>),
+                       dim3(grid), dim3(512), kLds, st, (const S*)A,
+                       (const S*)B, (const S*)B, (S*)C, offsets, N, K, NB, E,
+                       ncol, nseg, nullptr, Swiglu{}, Gather{}, kSplitUnits);
+    return hipGetLastError();
+  };
+  if (dt == DT_BF16) return go(std::integral_constant<int, DT_BF16>{});
+  return go(std::integral_constant<int, DT_F16>{});
 }
 
 hipError_t launch_experts_big(const void* xd, int dt, int64_t N, int64_t H,

@@ -139,6 +139,9 @@ hipError_t launch_grouped_nt(const void* A, int dt, int64_t N, int64_t K,
                              const uint32_t* offsets, void* C, hipStream_t st);
 // The prefill-sized kernel of launch_experts_big for a plain product (bf16
 // or f16; the same size limits).
+hipError_t launch_nn_big(const void* A, int dt, int64_t N, int K,
+                         const void* B, int NB, int E,
+                         const uint32_t* offsets, void* C, hipStream_t st);
 hipError_t launch_nt_big(const void* A, int dt, int64_t N, int K,
                          const void* B, int NB, int E,
                          const uint32_t* offsets, void* C, hipStream_t st);

@@ -160,7 +160,10 @@ def test_tiny_fp32():
     (300, 128, 256, 8, 2), (129, 128, 64, 16, 8),
     # weight gradients of several row blocks (M = 712 and 968: blocks of
     # 16-row units, the last unit half full) and ragged column blocks
-    (96, 968, 712, 4, 2)])
+    (96, 968, 712, 4, 2),
+    # N >= 96 E: the input gradients take the NN form (weights read K-major;
+    # K = 968 and 712 end inside a K step, NB inside a column block)
+    (400, 968, 712, 4, 2)])
 def test_ragged_bf16(T, H, I, E, k):
     wl = workloads.make("edge", T=T, H=H, I=I, E=E, k=k)
     wl["logits"] = torch.nan_to_num(wl["logits"].float(), nan=0.0,
@@ -181,6 +184,22 @@ def test_f16_with_idle_experts():
     _check_stages(r, "f16", "idle experts")
     for key in ("grad_w_gate", "grad_w_up", "grad_w_down"):
         assert torch.count_nonzero(r["b"][key][8:]) == 0
+
+
+def test_f16_nn_form():
+    """f16 chain at N >= 96 E, so the input gradients take the NN form
+    (the f16 instantiation), with one expert left without rows."""
+    wl = workloads.make("edge", T=400, H=136, I=200, E=4, k=2)
+    lg = wl["logits"].float()
+    lg[:, 3] = -30.0               # expert 3 gets no token
+    wl["logits"] = torch.nan_to_num(lg, nan=0.0, posinf=4.0,
+                                    neginf=-4.0).to(torch.float16)
+    for name in ("x", "w_gate", "w_up", "w_down"):
+        wl[name] = wl[name].to(torch.float16)
+    r = _run_chain(wl, 2, 5)
+    _check_stages(r, "f16", "f16 NN form")
+    for key in ("grad_w_gate", "grad_w_up", "grad_w_down"):
+        assert torch.count_nonzero(r["b"][key][3]) == 0
 
 
 def _bf16_edge(T, H, I, E, k):
