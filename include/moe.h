@@ -453,7 +453,8 @@ size_t moe_experts_backward_workspace_size(int64_t N, int64_t H, int64_t I,
  *   workspace   moe_experts_backward_workspace_size(N,H,I,E,dt) bytes,
  *               256-byte aligned.  It holds, in this order, each part at
  *               the next 256-byte aligned offset: one transposed weight
- *               tensor (E*H*I elements of dt), then dact, dgate_raw,
+ *               tensor (E*H*I elements of dt; written only for shapes the
+ *               K-major weight read does not take), then dact, dgate_raw,
  *               dup_raw [N,I] and the two input-gradient halves
  *               round(dgate_raw . w_gate[e]), round(dup_raw . w_up[e])
  *               [N,H], all dt; after the call dact .. the second half
