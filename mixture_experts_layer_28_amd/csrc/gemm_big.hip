@@ -351,21 +351,20 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   constexpr uint32_t OOB = 0x80000000u;
   const uint32_t rowbytes = (uint32_t)K * sizeof(S);
   // the A resource spans this tile's rows only (or, gathering, the token
-  // rows x [xrows, K], under 2^31 bytes), so every range fits in 31 bits
-  // and OOB (2^31) is always past the end; in the weight-gradient form B's
-  // resource spans the tile's columns only, too
+  // rows x [xrows, K], under 2^31 bytes; in the weight-gradient form, the
+  // expert's rows of the K-major operands), so every range fits in 31 bits
+  // and OOB (2^31) is always past the end
   const __amdgpu_buffer_rsrc_t rA =
       WG       ? make_rsrc(Ab, (uint64_t)K * (uint64_t)Mw * sizeof(S))
       : GATHER ? make_rsrc(A, (uint64_t)ga.xrows * rowbytes)
                : make_rsrc(Ab + row0 * K, (uint64_t)arows * rowbytes);
-  const int64_t bcols = NB - n0 < kBN ? NB - n0 : kBN;
   const __amdgpu_buffer_rsrc_t rB0 =
       WG ? make_rsrc(Bb, (uint64_t)K * (uint64_t)NB * sizeof(S))
          : make_rsrc(B0 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes);
   const __amdgpu_buffer_rsrc_t rB1 =
       GATEUP ? make_rsrc(B1 + (int64_t)e * NB * K, (uint64_t)NB * rowbytes)
              : rB0;
-  const int64_t boff = WG ? 0 : n0;  // B row of the tile's first column
+  const int64_t boff = n0;  // B row of the tile's first column
 
   const int wid = uniform(tid >> 6) & 7, lane = tid & 63;
   const int wm = wid / WN, wn = wid % WN;

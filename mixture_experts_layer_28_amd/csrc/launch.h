@@ -139,10 +139,12 @@ hipError_t launch_grouped_nt(const void* A, int dt, int64_t N, int64_t K,
                              const uint32_t* offsets, void* C, hipStream_t st);
 // The prefill-sized kernel of launch_experts_big for a plain product (bf16
 // or f16; the same size limits).
-hipError_t launch_nn_big(const void* A, int dt, int64_t N, int K,
+hipError_t launch_nt_big(const void* A, int dt, int64_t N, int K,
                          const void* B, int NB, int E,
                          const uint32_t* offsets, void* C, hipStream_t st);
-hipError_t launch_nt_big(const void* A, int dt, int64_t N, int K,
+// ... its NN form: C = A . B_e with B stored K-major ([E, K, NB]), read
+// through the LDS's transposing reads; the same types and limits.
+hipError_t launch_nn_big(const void* A, int dt, int64_t N, int K,
                          const void* B, int NB, int E,
                          const uint32_t* offsets, void* C, hipStream_t st);
 
@@ -175,11 +177,10 @@ hipError_t launch_experts_backward(
     const void* act, const void* dy, void* dxd, float* dwg, float* dwu,
     float* dwd, void* workspace, hipStream_t st);
 
-// Weight gradients on MFMA: Cw[e] [M, NC] FP32 = A_e . B_e^T where A_e
-// (A + (lo + 8e)*M) is [M, Kp] and B_e (B + (lo + 8e)*NC) is [NC, Kp] for
-// the rows [lo, lo + n_e) of expert e, Kp = n_e rounded up to a multiple of
-// 8 with zero padding (each expert's rows transposed into one block).
-// bf16/f16; M, NC multiples of 8; 16-byte aligned; 640 * (N + 8) < 2^31.
+// Weight gradients on MFMA: Cw[e] [M, NC] FP32 = A_e^T . B_e where A_e and
+// B_e are the rows [lo, lo + n_e) of expert e of A [N, M] and B [N, NC],
+// read in place (K-major, K = n_e).  bf16/f16; M, NC multiples of 8;
+// 16-byte aligned; N * max(M, NC) * 2 < 2^31.
 hipError_t launch_wgrad_big(const void* A, int dt, int64_t N, int M,
                             const void* B, int NC, int E,
                             const uint32_t* offsets, float* Cw,
